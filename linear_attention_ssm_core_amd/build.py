@@ -1,0 +1,57 @@
+"""Build libgdn.so (hand-written HIP kernels for gfx950 + the C ABI) in-tree.
+
+    python -m linear_attention_ssm_core_amd.build
+
+Every translation unit is compiled by hipcc for gfx950 only, with packed-fp32
+instruction selection disabled, then linked into
+linear_attention_ssm_core_amd/libgdn.so next to this file.
+"""
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OBJ_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgdn.so")
+
+SOURCES = ["api.cpp", "recurrent.hip", "conv_norm.hip", "prefill.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wextra",
+         "-Wno-unused-parameter", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", INCLUDE, "-I", CSRC]
+
+
+def _compile(src):
+    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (src, msgs))
+    return obj, msgs
+
+
+def build(verbose=False):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    for obj, msgs in results:
+        if verbose and msgs.strip():
+            print(msgs)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH] + [o for o, _ in results] + ["-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,318 @@
+// C ABI of libgdn.so (declared in include/gdn.h): argument validation and
+// dispatch to the kernel launchers.  Validation never touches the HIP runtime, so
+// a call with invalid arguments returns its status and launches nothing on any
+// machine.
+#include "gdn.h"
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace {
+
+using gdn::Geometry;
+
+bool dtype_ok(int32_t d) { return d == GDN_DTYPE_F32 || d == GDN_DTYPE_BF16; }
+
+gdn_status check_dims(const gdn_dims &d, int32_t act_dtype, int32_t out_dtype, Geometry *geo) {
+  if (!dtype_ok(act_dtype) || !dtype_ok(out_dtype)) return GDN_ERR_INVALID_ARG;
+  if (d.reserved != 0) return GDN_ERR_INVALID_ARG;
+  if (d.num_k_heads < 1 || d.num_v_heads < 1 || d.head_dim_k < 1 || d.head_dim_v < 1 ||
+      d.conv_kernel < 1)
+    return GDN_ERR_INVALID_ARG;
+  if (d.num_k_heads > 4096 || d.num_v_heads > 4096 || d.head_dim_k > 4096 || d.head_dim_v > 4096 ||
+      d.conv_kernel > 64)
+    return GDN_ERR_INVALID_ARG;
+  if (d.num_v_heads % d.num_k_heads != 0) return GDN_ERR_INVALID_ARG;
+  const int G = d.num_v_heads / d.num_k_heads;
+  if (G != 1 && G != 2 && G != 4) return GDN_ERR_UNSUPPORTED;
+  if (d.head_dim_k != d.head_dim_v) return GDN_ERR_UNSUPPORTED;
+  if (d.head_dim_k != 32 && d.head_dim_k != 64 && d.head_dim_k != 128) return GDN_ERR_UNSUPPORTED;
+  if (d.conv_kernel < 2 || d.conv_kernel > 4) return GDN_ERR_UNSUPPORTED;
+  geo->Hk = d.num_k_heads;
+  geo->Hv = d.num_v_heads;
+  geo->D = d.head_dim_k;
+  geo->K = d.conv_kernel;
+  geo->conv_dim = 2 * d.num_k_heads * d.head_dim_k + d.num_v_heads * d.head_dim_v;
+  geo->act_bf16 = act_dtype == GDN_DTYPE_BF16;
+  geo->out_bf16 = out_dtype == GDN_DTYPE_BF16;
+  return GDN_OK;
+}
+
+bool finite(float v) { return std::isfinite(v); }
+bool eps_ok(float v) { return std::isfinite(v) && v >= 0.0f; }
+
+gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+// Workspace layout of gdn_prefill_chunked: [front y (fp32, when x is given)]
+// [o staging (fp32, when z is given)] [chunk-kernel workspace].
+struct PrefillPlan {
+  Geometry geo;
+  bool fused_front, epilogue;
+  size_t y_bytes, o_bytes, core_bytes, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+gdn_status plan_prefill(const gdn_prefill_args *a, PrefillPlan *plan) {
+  if (a == nullptr) return GDN_ERR_INVALID_ARG;
+  if (a->struct_size != sizeof(gdn_prefill_args)) return GDN_ERR_INVALID_ARG;
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &plan->geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->total_tokens < 0 || a->reserved != 0 || a->reserved_f != 0.0f)
+    return GDN_ERR_INVALID_ARG;
+  if (a->chunk_size != GDN_PREFILL_CHUNK) return GDN_ERR_UNSUPPORTED;
+  if (a->total_tokens > ((int64_t)1 << 31) - 1) return GDN_ERR_INVALID_ARG;
+  if (a->total_tokens > 0 && a->num_seqs == 0) return GDN_ERR_INVALID_ARG;
+  if (!finite(a->scale) || !eps_ok(a->l2_eps) || !eps_ok(a->norm_eps)) return GDN_ERR_INVALID_ARG;
+  plan->fused_front = a->x != nullptr;
+  plan->epilogue = a->z != nullptr;
+  const int64_t T = a->total_tokens;
+  const Geometry &g = plan->geo;
+  plan->y_bytes = plan->fused_front ? align256((size_t)T * g.conv_dim * 4) : 0;
+  plan->o_bytes = plan->epilogue ? align256((size_t)T * g.Hv * g.D * 4) : 0;
+  plan->core_bytes = align256(gdn::prefill_core_workspace(g, a->num_seqs, T));
+  plan->total = plan->y_bytes + plan->o_bytes + plan->core_bytes;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gdn_status_string(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG: invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: no kernel for this shape";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown gdn_status";
+}
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+gdn_status gdn_conv_l2norm(const gdn_conv_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_conv_args)) return GDN_ERR_INVALID_ARG;
+  gdn::ConvLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->total_tokens < 0 || !eps_ok(a->l2_eps)) return GDN_ERR_INVALID_ARG;
+  if (a->total_tokens > ((int64_t)1 << 31) - 1) return GDN_ERR_INVALID_ARG;
+  if (a->total_tokens > 0 && a->num_seqs == 0) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 && (a->cu_seqlens == nullptr || a->conv_w == nullptr || a->conv_state == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  if (a->total_tokens > 0 && (a->x == nullptr || a->y == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (a->x != nullptr && a->x == a->y) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 65535) return GDN_ERR_INVALID_ARG;
+  p.n = a->num_seqs;
+  p.T = a->total_tokens;
+  p.cu = a->cu_seqlens;
+  p.x = a->x;
+  p.conv_w = a->conv_w;
+  p.conv_state = a->conv_state;
+  p.y = a->y;
+  p.y_f32 = 0;
+  p.l2_eps = a->l2_eps;
+  return hip_status(gdn::launch_conv_l2norm(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_decode_batched(const gdn_decode_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_decode_args)) return GDN_ERR_INVALID_ARG;
+  gdn::RecurrentLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->reserved_f != 0.0f) return GDN_ERR_INVALID_ARG;
+  if (!finite(a->scale) || !eps_ok(a->l2_eps) || !eps_ok(a->norm_eps)) return GDN_ERR_INVALID_ARG;
+  if ((int64_t)a->num_seqs * p.geo.Hk > ((int64_t)1 << 31) - 1) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 &&
+      (a->x == nullptr || a->conv_w == nullptr || a->conv_state == nullptr || a->a == nullptr ||
+       a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  p.n = a->num_seqs;
+  p.verify = 0;
+  p.cu = nullptr;
+  p.x = a->x;
+  p.conv_w = a->conv_w;
+  p.conv_state = a->conv_state;
+  p.a = a->a;
+  p.b = a->b;
+  p.states = a->h_state;
+  p.z = a->z;
+  p.norm_w = a->norm_w;
+  p.out = a->out;
+  p.scale = a->scale;
+  p.l2_eps = a->l2_eps;
+  p.norm_eps = a->norm_eps;
+  return hip_status(gdn::launch_recurrent(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_verify_multi(const gdn_verify_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_verify_args)) return GDN_ERR_INVALID_ARG;
+  gdn::RecurrentLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->num_seqs > GDN_VERIFY_WY_TABLE_SEQS) return GDN_ERR_INVALID_ARG;
+  if (a->max_k < GDN_VERIFY_MIN_K || a->max_k > GDN_VERIFY_MAX_K) return GDN_ERR_INVALID_ARG;
+  if (a->total_rows < 0 || a->total_rows > a->num_seqs * a->max_k) return GDN_ERR_INVALID_ARG;
+  if (a->reserved != 0 || a->reserved_f != 0.0f) return GDN_ERR_INVALID_ARG;
+  if (!finite(a->scale) || !eps_ok(a->l2_eps) || !eps_ok(a->norm_eps)) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 &&
+      (a->cu_ks == nullptr || a->x == nullptr || a->conv_w == nullptr || a->conv_state == nullptr ||
+       a->a == nullptr || a->b == nullptr || a->wy_tables == nullptr || a->out == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  p.n = a->num_seqs;
+  p.verify = 1;
+  p.cu = a->cu_ks;
+  p.x = a->x;
+  p.conv_w = a->conv_w;
+  p.conv_state = a->conv_state;
+  p.a = a->a;
+  p.b = a->b;
+  p.states = a->wy_tables;
+  p.z = a->z;
+  p.norm_w = a->norm_w;
+  p.out = a->out;
+  p.scale = a->scale;
+  p.l2_eps = a->l2_eps;
+  p.norm_eps = a->norm_eps;
+  return hip_status(gdn::launch_recurrent(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_verify_commit(const gdn_commit_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_commit_args)) return GDN_ERR_INVALID_ARG;
+  gdn::CommitLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, GDN_DTYPE_F32, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->num_seqs > GDN_VERIFY_WY_TABLE_SEQS || a->reserved != 0)
+    return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 && (a->cu_ks == nullptr || a->n_accepted == nullptr || a->wy_tables == nullptr ||
+                          a->x == nullptr || a->conv_state == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  p.n = a->num_seqs;
+  p.cu = a->cu_ks;
+  p.n_accepted = a->n_accepted;
+  p.tables = a->wy_tables;
+  p.x = a->x;
+  p.conv_state = a->conv_state;
+  return hip_status(gdn::launch_commit(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_gated_rmsnorm(const gdn_norm_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_norm_args)) return GDN_ERR_INVALID_ARG;
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->act_dtype) || !dtype_ok(a->out_dtype))
+    return GDN_ERR_INVALID_ARG;
+  const gdn_dims &d = a->dims;
+  if (d.num_v_heads < 1 || d.num_v_heads > 4096 || d.head_dim_v < 1 || a->total_tokens < 0 ||
+      a->reserved_f != 0.0f || !eps_ok(a->eps))
+    return GDN_ERR_INVALID_ARG;
+  if (d.head_dim_v != 32 && d.head_dim_v != 64 && d.head_dim_v != 128) return GDN_ERR_UNSUPPORTED;
+  if (a->total_tokens * d.num_v_heads > ((int64_t)1 << 33)) return GDN_ERR_INVALID_ARG;
+  if (a->total_tokens > 0 && (a->o == nullptr || a->z == nullptr || a->norm_w == nullptr || a->out == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  gdn::NormLaunch p{};
+  p.Hv = d.num_v_heads;
+  p.D = d.head_dim_v;
+  p.T = a->total_tokens;
+  p.in_bf16 = a->in_dtype == GDN_DTYPE_BF16;
+  p.act_bf16 = a->act_dtype == GDN_DTYPE_BF16;
+  p.out_bf16 = a->out_dtype == GDN_DTYPE_BF16;
+  p.o = a->o;
+  p.z = a->z;
+  p.norm_w = a->norm_w;
+  p.out = a->out;
+  p.eps = a->eps;
+  return hip_status(gdn::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_prefill_workspace_bytes(const gdn_prefill_args *a, size_t *bytes) {
+  if (bytes == nullptr) return GDN_ERR_INVALID_ARG;
+  *bytes = 0;
+  PrefillPlan plan;
+  gdn_status s = plan_prefill(a, &plan);
+  if (s != GDN_OK) return s;
+  *bytes = plan.total;
+  return GDN_OK;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
+  PrefillPlan plan;
+  gdn_status s = plan_prefill(a, &plan);
+  if (s != GDN_OK) return s;
+  const int n = a->num_seqs;
+  const int64_t T = a->total_tokens;
+  if (n > 0 && (a->cu_seqlens == nullptr || a->a == nullptr || a->b == nullptr || a->h_state == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  if (T > 0 && a->out == nullptr) return GDN_ERR_INVALID_ARG;
+  if (plan.fused_front && (a->conv_w == nullptr || a->conv_state == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!plan.fused_front && T > 0 && a->y == nullptr) return GDN_ERR_INVALID_ARG;
+  if (plan.epilogue && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  if (n > 65535) return GDN_ERR_INVALID_ARG;
+  if (plan.total > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.total))
+    return GDN_ERR_WORKSPACE;
+  if (n == 0) return GDN_OK;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(a->workspace);
+  const Geometry &g = plan.geo;
+
+  const void *y = a->y;
+  int y_bf16 = g.act_bf16;
+  if (plan.fused_front) {
+    gdn::ConvLaunch c{};
+    c.geo = g;
+    c.n = n;
+    c.T = T;
+    c.cu = a->cu_seqlens;
+    c.x = a->x;
+    c.conv_w = a->conv_w;
+    c.conv_state = a->conv_state;
+    c.y = ws;
+    c.y_f32 = 1;
+    c.l2_eps = a->l2_eps;
+    hipError_t e = gdn::launch_conv_l2norm(c, st);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+    y = ws;
+    y_bf16 = 0;
+  }
+  gdn::PrefillLaunch p{};
+  p.geo = g;
+  p.n = n;
+  p.T = T;
+  p.cu = a->cu_seqlens;
+  p.y = y;
+  p.y_bf16 = y_bf16;
+  p.a = a->a;
+  p.b = a->b;
+  p.h_state = a->h_state;
+  p.o = plan.epilogue ? static_cast<void *>(ws + plan.y_bytes) : a->out;
+  p.o_f32 = plan.epilogue ? 1 : 0;
+  p.scale = a->scale;
+  p.workspace = ws + plan.y_bytes + plan.o_bytes;
+  hipError_t e = gdn::launch_prefill(p, st);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  if (plan.epilogue && T > 0) {
+    gdn::NormLaunch nl{};
+    nl.Hv = g.Hv;
+    nl.D = g.D;
+    nl.T = T;
+    nl.in_bf16 = 0;
+    nl.act_bf16 = g.act_bf16;
+    nl.out_bf16 = g.out_bf16;
+    nl.o = p.o;
+    nl.z = a->z;
+    nl.norm_w = a->norm_w;
+    nl.out = a->out;
+    nl.eps = a->norm_eps;
+    e = gdn::launch_gated_rmsnorm(nl, st);
+    if (e != hipSuccess) return GDN_ERR_HIP;
+  }
+  return GDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Device helpers shared by the gfx950 kernels of libgdn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- scalar element access for the two activation dtypes --------------------
+__device__ __forceinline__ float ld(const float *p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld(const bf16 *p, size_t i) { return (float)p[i]; }
+__device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
+// float -> bf16 conversion rounds to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ void st(bf16 *p, size_t i, float v) { p[i] = (bf16)v; }
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// Sum over all 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Sum over the lanes that share (lane mod span); span is a power of two <= 64.
+template <int SPAN>
+__device__ __forceinline__ float sum_across_groups(float v) {
+#pragma unroll
+  for (int off = SPAN; off < kWave; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Sum over the first SPAN lanes' groups: lanes l and l^off for off < SPAN.
+template <int SPAN>
+__device__ __forceinline__ float sum_within_span(float v) {
+#pragma unroll
+  for (int off = SPAN / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// ---- bf16 hi/lo split of an fp32 value --------------------------------------
+// hi = x rounded to bf16, lo = (x - hi) rounded to bf16, so hi + lo carries about
+// 16 significant bits; products of split operands are taken as
+// hi*hi + hi*lo + lo*hi (the lo*lo term is below 2^-16 relative).
+__device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {
+  hi = (bf16)x;
+  lo = (bf16)(x - (float)hi);
+}
+
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16) on the matrix cores.
+// Lane l holds A row (l % 16), B column (l % 16), and the 8 k-elements of group
+// (l / 16); D lane l holds column (l % 16), rows 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ floatx4 mfma16(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace gdn

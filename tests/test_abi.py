@@ -1,0 +1,197 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+entry point, its structs match the ctypes mirror byte for byte, and invalid
+arguments are refused with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_ssm_core_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+FAKE = 0x1000  # never dereferenced: validation fails before any launch
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(gdn_[a-z0-9_]+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"gdn_conv_l2norm", "gdn_prefill_chunked", "gdn_decode_batched", "gdn_verify_multi",
+            "gdn_verify_commit", "gdn_gated_rmsnorm", "gdn_prefill_workspace_bytes",
+            "gdn_status_string", "gdn_abi_version"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for n in names:
+        assert n in exported, n
+        assert hasattr(B.library(), n)
+    assert B.abi_version() == 1
+
+
+def test_struct_layout_matches_header(tmp_path):
+    structs = ["gdn_dims", "gdn_conv_args", "gdn_prefill_args", "gdn_decode_args", "gdn_verify_args",
+               "gdn_commit_args", "gdn_norm_args"]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdn.h"', "int main(void) {"]
+    for s in structs:
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (s, s))
+        for f, _ in getattr(B, s)._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (s, f, s, f))
+    lines.append("return 0; }")
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.splitlines())
+    for s in structs:
+        cls = getattr(B, s)
+        assert int(got[s]) == ctypes.sizeof(cls), s
+        for f, _ in cls._fields_:
+            assert int(got["%s.%s" % (s, f)]) == getattr(cls, f).offset, (s, f)
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.status_string(s).startswith("GDN_")
+    assert "unknown" in B.status_string(99)
+
+
+def _dims(Hk=16, Hv=32, d=128, K=4):
+    return B.gdn_dims(Hk, Hv, d, d, K, 0)
+
+
+def _decode(**kw):
+    a = B.gdn_decode_args(ctypes.sizeof(B.gdn_decode_args), 1, 1, _dims(), 4, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, FAKE, None, None, FAKE, 1.0, 1e-6, 1e-6, 0.0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_decode_batched(ctypes.byref(a), None)
+
+
+def test_decode_validation():
+    assert _decode(struct_size=12) == B.GDN_ERR_INVALID_ARG
+    assert _decode(num_seqs=-1) == B.GDN_ERR_INVALID_ARG
+    assert _decode(x=None) == B.GDN_ERR_INVALID_ARG
+    assert _decode(h_state=None) == B.GDN_ERR_INVALID_ARG
+    assert _decode(z=FAKE) == B.GDN_ERR_INVALID_ARG          # z without norm_w
+    assert _decode(act_dtype=7) == B.GDN_ERR_INVALID_ARG
+    assert _decode(scale=float("nan")) == B.GDN_ERR_INVALID_ARG
+    assert _decode(l2_eps=-1.0) == B.GDN_ERR_INVALID_ARG
+    assert _decode(reserved_f=1.0) == B.GDN_ERR_INVALID_ARG
+    assert _decode(dims=_dims(d=96)) == B.GDN_ERR_UNSUPPORTED
+    assert _decode(dims=_dims(Hk=4, Hv=32)) == B.GDN_ERR_UNSUPPORTED   # 8 value heads per key head
+    assert _decode(dims=_dims(Hk=3, Hv=32)) == B.GDN_ERR_INVALID_ARG   # not a multiple
+    assert _decode(dims=B.gdn_dims(16, 32, 128, 64, 4, 0)) == B.GDN_ERR_UNSUPPORTED
+    assert _decode(dims=_dims(K=5)) == B.GDN_ERR_UNSUPPORTED
+    assert _decode(dims=B.gdn_dims(16, 32, 128, 128, 4, 1)) == B.GDN_ERR_INVALID_ARG
+    # nothing to do: accepted without touching the device
+    assert _decode(num_seqs=0, x=None, h_state=None) == B.GDN_OK
+    assert B.library().gdn_decode_batched(None, None) == B.GDN_ERR_INVALID_ARG
+
+
+def _verify(**kw):
+    a = B.gdn_verify_args(ctypes.sizeof(B.gdn_verify_args), 1, 1, _dims(), 64, 16, 576, 0, FAKE, FAKE,
+                          FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1.0, 1e-6, 1e-6, 0.0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_verify_multi(ctypes.byref(a), None)
+
+
+def test_verify_validation():
+    # tables are staged only for k in 2..16, at most 128 sequences (transformer_layer.rs page)
+    assert _verify(max_k=1) == B.GDN_ERR_INVALID_ARG
+    assert _verify(max_k=17) == B.GDN_ERR_INVALID_ARG
+    assert _verify(num_seqs=129) == B.GDN_ERR_INVALID_ARG
+    assert _verify(total_rows=64 * 16 + 1) == B.GDN_ERR_INVALID_ARG
+    assert _verify(wy_tables=None) == B.GDN_ERR_INVALID_ARG
+    assert _verify(cu_ks=None) == B.GDN_ERR_INVALID_ARG
+    assert _verify(reserved=3) == B.GDN_ERR_INVALID_ARG
+    assert _verify(dims=_dims(d=256)) == B.GDN_ERR_UNSUPPORTED
+    assert _verify(num_seqs=0, total_rows=0) == B.GDN_OK
+
+
+def _commit(**kw):
+    a = B.gdn_commit_args(ctypes.sizeof(B.gdn_commit_args), 1, _dims(), 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_verify_commit(ctypes.byref(a), None)
+
+
+def test_commit_validation():
+    assert _commit(num_seqs=129) == B.GDN_ERR_INVALID_ARG
+    assert _commit(n_accepted=None) == B.GDN_ERR_INVALID_ARG
+    assert _commit(struct_size=0) == B.GDN_ERR_INVALID_ARG
+    assert _commit(num_seqs=0) == B.GDN_OK
+
+
+def _conv(**kw):
+    a = B.gdn_conv_args(ctypes.sizeof(B.gdn_conv_args), 1, 1, _dims(), 8, 65536, FAKE, FAKE, FAKE, FAKE,
+                        FAKE + 64, 1e-6)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_conv_l2norm(ctypes.byref(a), None)
+
+
+def test_conv_validation():
+    assert _conv(y=FAKE) == B.GDN_ERR_INVALID_ARG          # y aliases x
+    assert _conv(num_seqs=0) == B.GDN_ERR_INVALID_ARG      # tokens without sequences
+    assert _conv(conv_state=None) == B.GDN_ERR_INVALID_ARG
+    assert _conv(l2_eps=float("inf")) == B.GDN_ERR_INVALID_ARG
+    assert _conv(total_tokens=0, x=None, y=None) == B.GDN_OK
+
+
+def _norm(**kw):
+    a = B.gdn_norm_args(ctypes.sizeof(B.gdn_norm_args), 0, 1, 1, _dims(), 100, FAKE, FAKE, FAKE, FAKE, 1e-6, 0.0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_gated_rmsnorm(ctypes.byref(a), None)
+
+
+def test_norm_validation():
+    assert _norm(z=None) == B.GDN_ERR_INVALID_ARG
+    assert _norm(in_dtype=2) == B.GDN_ERR_INVALID_ARG
+    assert _norm(eps=-1.0) == B.GDN_ERR_INVALID_ARG
+    assert _norm(dims=_dims(d=48)) == B.GDN_ERR_UNSUPPORTED
+    assert _norm(total_tokens=0, o=None) == B.GDN_OK
+
+
+def _prefill_args(**kw):
+    a = B.gdn_prefill_args(ctypes.sizeof(B.gdn_prefill_args), 1, 1, _dims(), 1, 4096, 64, 0, FAKE, FAKE,
+                           None, None, None, FAKE, FAKE, FAKE, None, None, FAKE, 1.0, 1e-6, 1e-6, 0.0,
+                           None, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _ws(a):
+    n = ctypes.c_size_t(0)
+    st = B.library().gdn_prefill_workspace_bytes(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def test_prefill_validation_and_workspace():
+    st, need = _ws(_prefill_args())
+    assert st == B.GDN_OK and need > 0
+    st_f, need_f = _ws(_prefill_args(x=FAKE, conv_w=FAKE, conv_state=FAKE))
+    st_e, need_e = _ws(_prefill_args(z=FAKE, norm_w=FAKE))
+    assert st_f == st_e == B.GDN_OK and need_f > need and need_e > need
+    L = B.library()
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(chunk_size=32)), None) == B.GDN_ERR_UNSUPPORTED
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args()), None) == B.GDN_ERR_WORKSPACE
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(workspace=FAKE, workspace_bytes=need - 1)),
+                                 None) == B.GDN_ERR_WORKSPACE
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(y=None)), None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(z=FAKE)), None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(x=FAKE)), None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(h_state=None)), None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(num_seqs=0)), None) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(reserved_f=2.0)), None) == B.GDN_ERR_INVALID_ARG
+    assert _ws(_prefill_args(dims=_dims(d=80)))[0] == B.GDN_ERR_UNSUPPORTED
+    ok = _prefill_args(num_seqs=0, total_tokens=0)
+    assert L.gdn_prefill_chunked(ctypes.byref(ok), None) == B.GDN_OK

@@ -1,0 +1,192 @@
+"""GPU parity of batched decode, verify, commit (through the C ABI) against the
+fp64 oracle, on the seeded workloads and their edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_ssm_core_amd import binding as B
+from linear_attention_ssm_core_amd import workloads as W
+from tests.gpu_util import (DEV, TOL_OUT, TOL_STATE, DeviceStates, act_dtype, host, row_seq_of, slice_err,
+                            tdev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_gpu(d, step, ds, out_dtype=torch.float32, with_norm=True, scale=1.0):
+    dims, act = d["dims"], act_dtype(d)
+    n = d["n"]
+    x = tdev(d["x"][step], act)
+    out = torch.empty((n, dims.Hv * dims.dv), dtype=out_dtype, device=DEV)
+    B.gdn_decode_batched(x, tdev(d["conv_w"], act), ds.ring_ptrs, tdev(d["a"][step], torch.float32),
+                         tdev(d["b"][step], torch.float32), ds.h_ptrs, out, dims,
+                         z=tdev(d["z"][step], act) if with_norm else None,
+                         norm_w=tdev(d["norm_w"], act) if with_norm else None, scale=scale)
+    return out
+
+
+def _decode_ref(d, step, S, ring, idx, with_norm=True, scale=1.0):
+    dims = d["dims"]
+    r = oracle.decode(d["x"][step][idx], d["conv_w"], ring, d["a"][step][idx], d["b"][step][idx], S,
+                      dims.Hk, dims.Hv, dims.dk, dims.dv, scale=scale,
+                      z=d["z"][step][idx] if with_norm else None, norm_w=d["norm_w"] if with_norm else None)
+    return (r["out"] if with_norm else r["o"]), r["S"], r["ring"]
+
+
+@pytest.mark.parametrize("with_norm", [False, True])
+def test_decode_tiny_fp32(with_norm):
+    """d = 32, 2 key / 4 value heads, fp32 everything, random states, 5 steps."""
+    d = W.decode_inputs(2000, 3, 5, W.TINY_DIMS, act="f32")
+    ds = DeviceStates(d["S0"], d["ring"], torch.float32)
+    S, ring = d["S0"].astype(np.float64), d["ring"].astype(np.float64)
+    idx = np.arange(3)
+    for step in range(5):
+        out = _decode_gpu(d, step, ds, with_norm=with_norm, scale=0.7)
+        ref, S, ring = _decode_ref(d, step, S, ring, idx, with_norm=with_norm, scale=0.7)
+        Hv, dv = d["dims"].Hv, d["dims"].dv
+        assert slice_err(host(out).reshape(3, Hv, dv), ref.reshape(3, Hv, dv), np.arange(3)) < TOL_OUT
+        assert slice_err(ds.h_host(), S) < TOL_STATE
+        assert np.array_equal(ds.ring_host(), ring)
+
+
+def test_decode_config2_100_steps():
+    """128 sequences x 100 consecutive steps, bf16 activations, fused conv/L2 and
+    gated-norm epilogue; outputs of every step and the final states checked on a
+    sample of 12 sequences (the GPU runs all 128)."""
+    d = W.config(2)
+    dims = d["dims"]
+    ds = DeviceStates(d["S0"], d["ring"], torch.bfloat16)
+    idx = np.array([0, 1, 17, 40, 63, 64, 77, 90, 101, 115, 126, 127])
+    S = d["S0"][idx].astype(np.float64)
+    ring = d["ring"][idx].astype(np.float64)
+    worst = 0.0
+    for step in range(d["steps"]):
+        out = _decode_gpu(d, step, ds)
+        ref, S, ring = _decode_ref(d, step, S, ring, idx)
+        g = host(out)[idx].reshape(len(idx), dims.Hv, dims.dv)
+        worst = max(worst, slice_err(g, ref.reshape(len(idx), dims.Hv, dims.dv), np.arange(len(idx))))
+    assert worst < TOL_OUT, worst
+    assert slice_err(ds.h_host()[idx], S) < TOL_STATE
+    assert np.array_equal(ds.ring_host()[idx], ring)
+
+
+def test_decode_identity_and_bf16_store():
+    """a = 1, b = 0 leaves every state bitwise unchanged; a bf16 output is the
+    round-to-nearest-even of the fp32 output of the same step."""
+    d = W.decode_inputs(2001, 16, 1, W.QWEN_DIMS)
+    d["a"][:] = 1.0
+    d["b"][:] = 0.0
+    ds = DeviceStates(d["S0"], d["ring"], torch.bfloat16)
+    before = ds.h_host()
+    rings = [r.clone() for r in ds.ring]
+    out32 = _decode_gpu(d, 0, ds, torch.float32)
+    assert np.array_equal(ds.h_host(), before)
+    for r, r0 in zip(ds.ring, rings):   # restore the conv state for the second run
+        r.copy_(r0)
+    out16 = _decode_gpu(d, 0, ds, torch.bfloat16)
+    assert torch.equal(out32.to(torch.bfloat16), out16)
+
+
+def test_decode_deterministic():
+    d = W.decode_inputs(2002, 32, 1, W.QWEN_DIMS)
+    res = []
+    for _ in range(2):
+        ds = DeviceStates(d["S0"], d["ring"], torch.bfloat16)
+        out = _decode_gpu(d, 0, ds)
+        res.append((out.clone(), [h.clone() for h in ds.h]))
+    assert torch.equal(res[0][0], res[1][0])
+    assert all(torch.equal(a, b) for a, b in zip(res[0][1], res[1][1]))
+
+
+def _verify_setup(d):
+    dims = d["dims"]
+    act = act_dtype(d)
+    n = d["n"]
+    ks = d["ks"]
+    ds = DeviceStates(d["S0"], d["ring"], act)
+    inter = [[torch.full((dims.Hv, dims.dk, dims.dv), float("nan"), device=DEV) for _ in range(ks[i] - 1)]
+             for i in range(n)]
+    tables = [[None] * n for _ in range(16)]
+    for i in range(n):
+        tables[0][i] = ds.h[i]
+        for t in range(ks[i] - 1):
+            tables[t + 1][i] = inter[i][t]
+    tab = B.wy_tables(tables, DEV)
+    return ds, inter, tab
+
+
+def _verify_gpu(d, ds, tab, out_dtype=torch.float32, with_norm=True):
+    dims, act = d["dims"], act_dtype(d)
+    T = int(d["cu"][-1])
+    out = torch.empty((T, dims.Hv * dims.dv), dtype=out_dtype, device=DEV)
+    B.gdn_verify_multi(tdev(d["x"], act), tdev(d["conv_w"], act), ds.ring_ptrs, tdev(d["a"], torch.float32),
+                       tdev(d["b"], torch.float32), tab, tdev(d["cu"], torch.int32), int(max(2, d["ks"].max())),
+                       out, dims, z=tdev(d["z"], act) if with_norm else None,
+                       norm_w=tdev(d["norm_w"], act) if with_norm else None)
+    return out
+
+
+@pytest.mark.parametrize("case", ["config3", "tiny_fp32", "edge_k"])
+def test_verify_and_commit(case):
+    if case == "config3":
+        d = W.config(3)
+        sample = np.array([0, 3, 11, 31, 47, 63])
+    elif case == "tiny_fp32":
+        d = W.verify_inputs(3001, 5, W.TINY_DIMS, act="f32")
+        sample = np.arange(5)
+    else:  # k = 1, 2 and 16, and the widest batch (128 sequences)
+        ks = np.array(([1, 2, 16] * 43)[:128])
+        d = W.verify_inputs(3002, 128, W.QWEN_DIMS, ks=ks)
+        sample = np.array([0, 1, 2, 64, 125, 126, 127])
+    dims = d["dims"]
+    cu, ks, n = d["cu"], d["ks"], d["n"]
+    ds, inter, tab = _verify_setup(d)
+    ring_before = ds.ring_host()
+    out = _verify_gpu(d, ds, tab)
+    assert np.array_equal(ds.ring_host(), ring_before)  # verify only reads the conv state
+
+    # oracle on the sampled sequences
+    rows = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in sample])
+    cu_s = np.concatenate([[0], np.cumsum(ks[sample])]).astype(np.int32)
+    ref = oracle.verify(d["x"][rows], d["conv_w"], d["ring"][sample], d["a"][rows], d["b"][rows],
+                        d["S0"][sample], cu_s, dims.Hk, dims.Hv, dims.dk, dims.dv, z=d["z"][rows],
+                        norm_w=d["norm_w"])
+    g = host(out)[rows].reshape(len(rows), dims.Hv, dims.dv)
+    assert slice_err(g, ref["out"], row_seq_of(cu_s)) < TOL_OUT
+    # intermediate states S_t in table t+1, the last one in table 0
+    worst = 0.0
+    for j, i in enumerate(sample):
+        for t in range(ks[i]):
+            gpu_state = host(inter[i][t]) if t < ks[i] - 1 else host(ds.h[i])
+            worst = max(worst, slice_err(gpu_state[None], ref["states"][cu_s[j] + t][None]))
+    assert worst < TOL_STATE, worst
+
+    # commit a random accepted prefix
+    n_acc = d["n_acc"]
+    B.gdn_verify_commit(tdev(d["x"], act_dtype(d)), ds.ring_ptrs, tab, tdev(cu, torch.int32),
+                        torch.from_numpy(n_acc).to(DEV), dims)
+    S_c, ring_c = oracle.commit(ref["states"], n_acc[sample], cu_s, d["ring"][sample], d["x"][rows])
+    assert slice_err(ds.h_host()[sample], S_c) < TOL_STATE
+    assert np.array_equal(ds.ring_host()[sample], ring_c)
+
+
+def test_verify_matches_decode_steps_bitwise_state():
+    """A verify of k rows from S_0 ends in the same state (to fp32 rounding order,
+    within the state tolerance) as k one-token decode steps; commit(n_i = 1) equals
+    one decode step."""
+    d = W.verify_inputs(3003, 4, W.QWEN_DIMS, ks=[4, 4, 4, 4])
+    dims = d["dims"]
+    ds, inter, tab = _verify_setup(d)
+    _verify_gpu(d, ds, tab, with_norm=False)
+    dd = W.decode_inputs(0, 4, 1, W.QWEN_DIMS)
+    dd.update(S0=d["S0"], ring=d["ring"], conv_w=d["conv_w"], norm_w=d["norm_w"])
+    ds2 = DeviceStates(d["S0"], d["ring"], torch.bfloat16)
+    for t in range(4):
+        rows = d["cu"][:-1] + t
+        dd["x"] = d["x"][rows][None]
+        dd["a"] = d["a"][rows][None]
+        dd["b"] = d["b"][rows][None]
+        _decode_gpu(dd, 0, ds2, with_norm=False)
+        for i in range(4):
+            gs = host(inter[i][t]) if t < 3 else host(ds.h[i])
+            assert slice_err(gs[None], host(ds2.h[i])[None]) < 1e-5
