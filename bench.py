@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Throughput of the GDN mixer core on one MI355X.
+
+One step is one pass of the whole hot path over synthetic inputs resident in HBM:
+
+  prefill  T = 4096 tokens, 16 key / 32 value heads, d = 128, bf16 activations,
+           fp32 state: gdn_conv_l2norm -> gdn_prefill_chunked -> gdn_gated_rmsnorm
+  decode   128 sequences x 100 consecutive steps of gdn_decode_batched (fused
+           conv/L2 prologue and gated-norm epilogue, fp32 states in place)
+  verify   64 sequences, draft lengths k ~ U{2..16}: gdn_verify_multi writing every
+           intermediate state through the WY tables, then gdn_verify_commit
+
+value = tokens processed per step / step time (prefill tokens + decode
+sequence-tokens + verify rows).  The JSON line also carries per-phase figures,
+the roofline of the dominant kernel (from HIP events around each of its
+launches) and the fp64 CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calib    # plain 1 GiB copy, to scale HBM counters
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15     # FLOP/s, MI355X dense bf16
+
+D, HK, HV, C = 128, 16, 32, 64
+STATE_BYTES = HV * D * D * 4            # one sequence's fp32 state, 2 MiB
+CONV_DIM = 2 * HK * D + HV * D          # 8192
+
+
+def decode_bytes_per_seq():
+    """Algorithmic HBM bytes of one sequence-token of batched decode."""
+    return (2 * STATE_BYTES            # state read + written
+            + CONV_DIM * 2             # x row (bf16)
+            + 2 * 3 * CONV_DIM * 2     # conv state read + written
+            + HV * D * 2               # z (bf16)
+            + HV * D * 2               # out (bf16)
+            + 2 * HV * 4)              # a, b
+
+
+def verify_bytes(ks):
+    per_seq = STATE_BYTES * (1 + ks) + 3 * CONV_DIM * 2
+    per_row = CONV_DIM * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4
+    return int(np.sum(per_seq) + per_row * np.sum(ks)) + CONV_DIM * 4 * 2
+
+
+def prefill_flops_per_token():
+    return HV * (6 * D * D + C * D + 2 * C * D + C * C / 3.0) + HK * (2 * C * D)
+
+
+def prefill_bytes(T):
+    # q_hat, k_hat, v in (bf16), out (bf16), a, b, plus the state read and written
+    return T * (CONV_DIM * 2 + HV * D * 2 + 2 * HV * 4) + 2 * STATE_BYTES
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    return ap.parse_args()
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
+
+
+class Workloads:
+    """Device buffers for the three phases, filled from the seeded generator."""
+
+    def __init__(self, torch, B, W):
+        dev = "cuda"
+        bf, f32 = torch.bfloat16, torch.float32
+        t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+        self.dims = W.QWEN_DIMS
+        # prefill (T = 4096)
+        p = W.config(1)
+        self.p_T = int(p["cu"][-1])
+        self.p_cu = t(p["cu"], torch.int32)
+        self.p_x = t(p["x"], bf)
+        self.p_z = t(p["z"], bf)
+        self.p_a = t(p["a"], f32)
+        self.p_b = t(p["b"], f32)
+        self.p_w = t(p["conv_w"], bf)
+        self.p_nw = t(p["norm_w"], bf)
+        self.p_h = [t(p["S0"][i], f32) for i in range(p["S0"].shape[0])]
+        self.p_ring = [t(p["ring"][i], bf) for i in range(p["ring"].shape[0])]
+        self.p_hp, self.p_rp = B.ptr_array(self.p_h), B.ptr_array(self.p_ring)
+        self.p_y = torch.empty((self.p_T, CONV_DIM), dtype=bf, device=dev)
+        self.p_o = torch.empty((self.p_T, HV * D), dtype=bf, device=dev)
+        self.p_out = torch.empty((self.p_T, HV * D), dtype=bf, device=dev)
+        nb = B.gdn_prefill_workspace_bytes(self.dims, self.p_cu, self.p_a, self.p_b, self.p_hp, self.p_o,
+                                           y=self.p_y)
+        self.p_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        # decode (128 sequences x 100 steps)
+        d = W.config(2)
+        self.d_n, self.d_steps = d["n"], d["steps"]
+        self.d_x = t(d["x"], bf)
+        self.d_z = t(d["z"], bf)
+        self.d_a = t(d["a"], f32)
+        self.d_b = t(d["b"], f32)
+        self.d_w = t(d["conv_w"], bf)
+        self.d_nw = t(d["norm_w"], bf)
+        self.d_h = [t(d["S0"][i], f32) for i in range(self.d_n)]
+        self.d_ring = [t(d["ring"][i], bf) for i in range(self.d_n)]
+        self.d_hp, self.d_rp = B.ptr_array(self.d_h), B.ptr_array(self.d_ring)
+        self.d_out = torch.empty((self.d_n, HV * D), dtype=bf, device=dev)
+        # verify (64 sequences, k ~ U{2..16}) and commit
+        v = W.config(3)
+        self.v_n, self.v_ks = v["n"], v["ks"].astype(np.int64)
+        self.v_rows = int(v["cu"][-1])
+        self.v_cu = t(v["cu"], torch.int32)
+        self.v_x = t(v["x"], bf)
+        self.v_z = t(v["z"], bf)
+        self.v_a = t(v["a"], f32)
+        self.v_b = t(v["b"], f32)
+        self.v_w = t(v["conv_w"], bf)
+        self.v_nw = t(v["norm_w"], bf)
+        self.v_h = [t(v["S0"][i], f32) for i in range(self.v_n)]
+        self.v_ring = [t(v["ring"][i], bf) for i in range(self.v_n)]
+        self.v_rp = B.ptr_array(self.v_ring)
+        self.v_inter = [[torch.empty((HV, D, D), dtype=f32, device=dev) for _ in range(k - 1)] for k in self.v_ks]
+        tables = [[None] * self.v_n for _ in range(16)]
+        for i in range(self.v_n):
+            tables[0][i] = self.v_h[i]
+            for j, buf in enumerate(self.v_inter[i]):
+                tables[j + 1][i] = buf
+        self.v_tab = B.wy_tables(tables, dev)
+        self.v_out = torch.empty((self.v_rows, HV * D), dtype=bf, device=dev)
+        self.v_nacc = t(v["n_acc"], torch.int32)
+        self.v_maxk = int(self.v_ks.max())
+        self.tokens_per_step = self.p_T + self.d_n * self.d_steps + self.v_rows
+
+
+def run_step(torch, B, w, ev=None):
+    """One pass of the hot path.  ev: dict of lists that receives HIP events."""
+    rec = (lambda key: ev[key].append(_event(torch))) if ev is not None else (lambda key: None)
+    dims = w.dims
+    rec("p0")
+    B.gdn_conv_l2norm(w.p_x, w.p_w, w.p_rp, w.p_cu, w.p_y, dims)
+    rec("p1")
+    B.gdn_prefill_chunked(dims, w.p_cu, w.p_a, w.p_b, w.p_hp, w.p_o, y=w.p_y, workspace=w.p_ws)
+    rec("p2")
+    B.gdn_gated_rmsnorm(w.p_o, w.p_z, w.p_nw, w.p_out, dims)
+    rec("p3")
+    for s in range(w.d_steps):
+        rec("d0")
+        B.gdn_decode_batched(w.d_x[s], w.d_w, w.d_rp, w.d_a[s], w.d_b[s], w.d_hp, w.d_out, dims,
+                             z=w.d_z[s], norm_w=w.d_nw)
+        rec("d1")
+    rec("v0")
+    B.gdn_verify_multi(w.v_x, w.v_w, w.v_rp, w.v_a, w.v_b, w.v_tab, w.v_cu, w.v_maxk, w.v_out, dims,
+                       z=w.v_z, norm_w=w.v_nw)
+    rec("v1")
+    B.gdn_verify_commit(w.v_x, w.v_rp, w.v_tab, w.v_cu, w.v_nacc, dims)
+    rec("v2")
+
+
+def _event(torch):
+    e = torch.cuda.Event(enable_timing=True)
+    e.record(torch.cuda.current_stream())
+    return e
+
+
+def _pair_ms(a, b):
+    return [x.elapsed_time(y) for x, y in zip(a, b)]
+
+
+def cpu_baseline(W):
+    """The fp64 oracle, as it stands, on a bounded sample of each phase; each
+    phase's time is scaled to the step's token count."""
+    import oracle
+    dims = W.QWEN_DIMS
+    threads = oracle.num_threads()
+    t_total = 0.0
+    # prefill: all 32 heads, first 1024 of the 4096 tokens
+    p = W.config(1)
+    Tp = 1024
+    cu = np.array([0, Tp], dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.prefill(p["x"][:Tp], p["a"][:Tp], p["b"][:Tp], p["S0"], cu, dims.Hk, dims.Hv, dims.dk, dims.dv,
+                   conv_w=p["conv_w"], ring=p["ring"], z=p["z"][:Tp], norm_w=p["norm_w"])
+    t_pre = (time.perf_counter() - t0) * (4096 / Tp)
+    # decode: 48 of 128 sequences, 10 of 100 steps
+    d = W.config(2, steps=10)
+    ns, steps = 48, 10
+    S, ring = d["S0"][:ns], d["ring"][:ns]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        r = oracle.decode(d["x"][s][:ns], d["conv_w"], ring, d["a"][s][:ns], d["b"][s][:ns], S, dims.Hk,
+                          dims.Hv, dims.dk, dims.dv, z=d["z"][s][:ns], norm_w=d["norm_w"])
+        S, ring = r["S"], r["ring"]
+    t_dec = (time.perf_counter() - t0) * (128 / ns) * (100 / steps)
+    # verify: 24 of 64 sequences (all of their rows), then commit
+    v = W.config(3)
+    sel = np.arange(24)
+    rows = np.concatenate([np.arange(v["cu"][i], v["cu"][i + 1]) for i in sel])
+    cu_s = np.concatenate([[0], np.cumsum(v["ks"][sel])]).astype(np.int32)
+    t0 = time.perf_counter()
+    ref = oracle.verify(v["x"][rows], v["conv_w"], v["ring"][sel], v["a"][rows], v["b"][rows], v["S0"][sel],
+                        cu_s, dims.Hk, dims.Hv, dims.dk, dims.dv, z=v["z"][rows], norm_w=v["norm_w"])
+    oracle.commit(ref["states"], v["n_acc"][sel], cu_s, v["ring"][sel], v["x"][rows])
+    t_ver = (time.perf_counter() - t0) * (int(v["cu"][-1]) / len(rows))
+    t_total = t_pre + t_dec + t_ver
+    tokens = 4096 + 128 * 100 + int(v["cu"][-1])
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle (C, OpenMP over sequence x value head) on: prefill of the first 1024 of "
+                      "4096 tokens (all 32 heads, conv front and gated norm), decode of 48 of 128 sequences "
+                      "for 10 of 100 steps, verify + commit of 24 of 64 sequences; each phase's time scaled "
+                      "to the full step (%d tokens)" % tokens,
+            "phase_seconds_scaled": {"prefill": t_pre, "decode": t_dec, "verify": t_ver}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import torch
+    if args.copy_calib:
+        copy_calibration(torch)
+        return
+    from linear_attention_ssm_core_amd import binding as B
+    from linear_attention_ssm_core_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    w = Workloads(torch, B, W)
+    print("bench: inputs resident; warmup %d, timed %d steps" % (args.warmup, args.steps), file=sys.stderr,
+          flush=True)
+    for _ in range(args.warmup):
+        run_step(torch, B, w)
+    torch.cuda.synchronize()
+
+    keys = ["p0", "p1", "p2", "p3", "d0", "d1", "v0", "v1", "v2"]
+    ev = {k: [] for k in keys}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        run_step(torch, B, w, ev)
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+
+    conv_ms = np.mean(_pair_ms(ev["p0"], ev["p1"]))
+    pre_ms = np.mean(_pair_ms(ev["p1"], ev["p2"]))
+    norm_ms = np.mean(_pair_ms(ev["p2"], ev["p3"]))
+    dec_ms = np.array(_pair_ms(ev["d0"], ev["d1"]))
+    ver_ms = np.mean(_pair_ms(ev["v0"], ev["v1"]))
+    com_ms = np.mean(_pair_ms(ev["v1"], ev["v2"]))
+
+    dec_bytes = w.d_n * decode_bytes_per_seq() + CONV_DIM * 4 * 2 + D * 2
+    dec_avg_s = float(np.mean(dec_ms)) / 1e3
+    dec_gbs = dec_bytes / dec_avg_s / 1e9
+    ver_bytes = verify_bytes(w.v_ks)
+    pre_flops = prefill_flops_per_token() * w.p_T
+    phases = {
+        "prefill": {"tokens": w.p_T, "ms_chain": conv_ms + pre_ms + norm_ms, "ms_conv_l2norm": conv_ms,
+                    "ms_prefill_chunked": pre_ms, "ms_gated_rmsnorm": norm_ms,
+                    "tokens_per_s": w.p_T / ((conv_ms + pre_ms + norm_ms) / 1e3),
+                    "prefill_chunked_tflops": pre_flops / (pre_ms / 1e3) / 1e12,
+                    "mfma_frac": pre_flops / (pre_ms / 1e3) / MFMA_BF16_PEAK,
+                    "hbm_frac": prefill_bytes(w.p_T) / (pre_ms / 1e3) / HBM_PEAK},
+        "decode": {"seq_tokens": w.d_n * w.d_steps, "ms_per_launch": float(np.mean(dec_ms)),
+                   "tokens_per_s": w.d_n / dec_avg_s, "gb_per_s": dec_gbs, "hbm_frac": dec_gbs * 1e9 / HBM_PEAK},
+        "verify": {"rows": w.v_rows, "ms": ver_ms, "tokens_per_s": w.v_rows / (ver_ms / 1e3),
+                   "gb_per_s": ver_bytes / (ver_ms / 1e3) / 1e9,
+                   "hbm_frac": ver_bytes / (ver_ms / 1e3) / HBM_PEAK},
+        "commit": {"ms": com_ms},
+    }
+    line = {
+        "metric": "GDN tokens/s: prefill (MFMA %) + batched decode/verify (HBM GB/s %), 1 GPU",
+        "value": w.tokens_per_step / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes of the five GDN workloads)",
+        "config": {"workload": "GDN mixer core step: prefill T=4096 (16/32 heads, d=128, chunk 64) + "
+                               "batched decode 128 seqs x 100 steps + speculative verify/commit 64 seqs "
+                               "k~U{2..16}", "tokens_per_step": w.tokens_per_step,
+                   "verify_rows": w.v_rows},
+        "roofline": {"bound": "hbm", "kernel": "gdn_decode_batched (recurrent_kernel<128,2,1>)",
+                     "achieved": dec_gbs, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": dec_gbs * 1e9 / HBM_PEAK, "traffic": None,
+                     "bytes_per_launch": dec_bytes, "avg_launch_ms": float(np.mean(dec_ms)),
+                     "launches_timed": int(dec_ms.size)},
+        "phases": phases,
+        "wall_s_timed": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(W)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
