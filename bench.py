@@ -171,6 +171,24 @@ def run_step(torch, B, w, ev=None):
     rec("v2")
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
+    """Attainable read+write bandwidth of a plain device copy (torch), GB/s."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
 def _event(torch):
     e = torch.cuda.Event(enable_timing=True)
     e.record(torch.cuda.current_stream())
@@ -311,6 +329,8 @@ def main():
                      "bytes_per_launch": dec_bytes, "avg_launch_ms": float(np.mean(dec_ms)),
                      "launches_timed": int(dec_ms.size)},
         "phases": phases,
+        "attainable": {"copy_gb_per_s": copy_bandwidth(torch),
+                       "note": "plain 1 GiB device-to-device copy (read + write bytes / time)"},
         "wall_s_timed": t_wall,
     }
     if not args.no_cpu_baseline:

@@ -54,7 +54,15 @@ constexpr int kLP = 72;    // padded LDS row (bf16 elements) of [*][64] tiles
 
 __host__ __device__ constexpr size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 int64_t max_chunks(int n, int64_t T) { return T / kC + n; }
+// Per (chunk, value head): E and MT as bf16 hi/lo planes in MFMA A-fragment order
+// ([tile][k-step][lane][8]: one wave-wide 16-byte load is one contiguous 1 KiB
+// block), then Gam[64].
 __host__ __device__ constexpr size_t unit_bytes(int D) { return a256((size_t)4 * D * kC + (size_t)4 * kC * kC + 256); }
+// Per (chunk, key head): K and Q rows in A-fragment order ([row block][k-step][lane][8]),
+// np planes (hi, and lo for fp32 activations).
+__host__ __device__ constexpr size_t kq_bytes(int D, int np) { return a256((size_t)2 * np * kC * D * 2); }
+// Element offset of lane `lane`'s 8 values of fragment (tile, ks) with nks k-steps.
+__host__ __device__ constexpr int frag_off(int tile, int ks, int nks, int lane) { return ((tile * nks + ks) * 64 + lane) * 8; }
 
 struct Tables {
   int32_t *seq_chunk0;   // [n+1] first chunk of each sequence
@@ -88,17 +96,15 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 
 // 8 consecutive activations as an MFMA operand: bf16 storage is exact (lo unused),
-// fp32 storage is split into hi + lo.
-__device__ __forceinline__ void frag8(const bf16 *p, bool valid, bf16x8 &hi, bf16x8 &lo) {
-  hi = valid ? *reinterpret_cast<const bf16x8 *>(p) : zero8();
+// fp32 storage is split into hi + lo.  Loads are unconditional: callers clamp the
+// row into the chunk, and rows past the chunk end only ever meet exact zeros
+// (T has zero rows and columns for them), so no exec-masked load -- and no
+// waitcnt that would drain the next chunk's prefetch -- is needed.
+__device__ __forceinline__ void frag8(const bf16 *p, bf16x8 &hi, bf16x8 &lo) {
+  hi = *reinterpret_cast<const bf16x8 *>(p);
   lo = zero8();
 }
-__device__ __forceinline__ void frag8(const float *p, bool valid, bf16x8 &hi, bf16x8 &lo) {
-  if (!valid) {
-    hi = zero8();
-    lo = zero8();
-    return;
-  }
+__device__ __forceinline__ void frag8(const float *p, bf16x8 &hi, bf16x8 &lo) {
   const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -134,27 +140,29 @@ __device__ __forceinline__ void store_split4(bf16 *hi, bf16 *lo, const float v[4
 
 // ---- 1. chunk table ----------------------------------------------------------
 __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t *cu, int n, int64_t NC, Tables tb) {
-  __shared__ int32_t s_part[256];
-  __shared__ int32_t s_total;
-  const int tid = threadIdx.x;
+  __shared__ int32_t s_wave[4];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int per = (n + 255) / 256;
   const int s0 = min(n, tid * per), s1 = min(n, s0 + per);
   int local = 0;
   for (int s = s0; s < s1; ++s) local += (cu[s + 1] - cu[s] + kC - 1) / kC;
-  s_part[tid] = local;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int k = 0; k < 256; ++k) {
-      const int v = s_part[k];
-      s_part[k] = acc;
-      acc += v;
-    }
-    s_total = acc;
-    tb.seq_chunk0[n] = acc;
+  // block-wide exclusive scan of the per-thread chunk counts
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
   }
+  if (lane == kWave - 1) s_wave[wave] = incl;
   __syncthreads();
-  int run = s_part[tid];
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    base += (w < wave) ? s_wave[w] : 0;
+    total += s_wave[w];
+  }
+  int run = base + incl - local;
+  if (tid == 0) tb.seq_chunk0[n] = total;
   for (int s = s0; s < s1; ++s) {
     tb.seq_chunk0[s] = run;
     const int len = cu[s + 1] - cu[s];
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t *cu, int
     }
     run += nc;
   }
-  for (int64_t idx = s_total + tid; idx < NC; idx += 256) tb.chunk_seq[idx] = -1;
+  for (int64_t idx = total + tid; idx < NC; idx += 256) tb.chunk_seq[idx] = -1;
   // longest sequences first (rank sort; identity order for very large batches)
   for (int s = tid; s < n; s += 256) {
     if (n <= 4096) {
@@ -184,19 +192,37 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t *cu, int
 }
 
 // ---- 2. per-chunk UT transform -------------------------------------------------
+// acc += A(16x16) * B(16x16) with fp32 operands from LDS (row strides lda, ldb),
+// as four fp32 MFMAs of k = 4.  Lane l supplies A[l%16][4kk + l/16] and
+// B[4kk + l/16][l%16]; the result is in the usual 16x16 D layout.
+__device__ __forceinline__ floatx4 mm16_f32(const float *A, int lda, const float *B, int ldb, floatx4 acc, int lr,
+                                            int lg) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[lr * lda + 4 * kk + lg], B[(4 * kk + lg) * ldb + lr], acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ void store_tile(float *dst, int ld, const floatx4 &v, float sgn, int lr, int lg) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) dst[(4 * lg + rr) * ld + lr] = sgn * v[rr];
+}
+
 template <int D, typename TY>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, char *units) {
   constexpr bool SP = std::is_same<TY, float>::value;
   constexpr int NP = SP ? 2 : 1;
   constexpr int KS = D / 32;
   constexpr int NTI = D / 16;
+  constexpr int LF = kC + 1;  // fp32 LDS row stride
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   const int cidx = blockIdx.x / Hv, h = blockIdx.x - cidx * Hv;
   const int seq = tb.chunk_seq[cidx];
   if (seq < 0) return;
   const int t0 = tb.chunk_start[cidx], L = tb.chunk_len[cidx];
   const int g = h / G;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave, lr = lane % 16, lg = lane / 16;
+  const int tid = threadIdx.x, lane = tid % kWave, lr = lane % 16, lg = lane / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const TY *y = static_cast<const TY *>(p.y);
   const TY *Qb = y + (size_t)t0 * CD + (size_t)g * D;
   const TY *Kb = y + (size_t)t0 * CD + (size_t)(Hk + g) * D;
@@ -211,18 +237,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   __shared__ float s_gam[kC], s_bb[kC], s_dec[kC];
   __shared__ __align__(16) bf16 s_Kt[NP][D][kLP];    // K^T, B operand of E
   __shared__ __align__(16) bf16 s_M[2][kC][kLP];     // M hi/lo, row-major
-  __shared__ __align__(16) float s_T[kC][kC + 1];    // T, fp32
-  __shared__ __align__(16) float s_A[kC][kC + 1];    // Abar, fp32
-  __shared__ float s_Li[4][16][17];                  // inverses of the diagonal blocks of I + Abar
-  __shared__ float s_P[3][16][17];
+  __shared__ __align__(16) float s_A[kC][LF];        // Abar (L = I + Abar), fp32
+  __shared__ __align__(16) float s_L[kC][LF];        // L^-1, fp32
+  __shared__ __align__(16) float s_Y[4][16][17];     // product scratch
 
-  // ---- A: gates and K^T staging ----
+  // ---- A: gates; K^T staging and the phase-B fragments, all loads up front ----
   if (wave == 0) {
-    float la = 0.0f, bb = 0.0f;
-    if (lane < L) {
-      la = fmaxf(logf(p.a[(size_t)(t0 + lane) * Hv + h]), -30.0f);
-      bb = p.b[(size_t)(t0 + lane) * Hv + h];
-    }
+    const size_t gi = (size_t)(t0 + min(lane, L - 1)) * Hv + h;
+    const float a_raw = p.a[gi], b_raw = p.b[gi];
+    float la = (lane < L) ? fmaxf(logf(a_raw), -30.0f) : 0.0f;
+    const float bb = (lane < L) ? b_raw : 0.0f;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const float v = __shfl_up(la, off);
@@ -234,56 +258,69 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     s_dec[lane] = expf(glast - la);
     Gam[lane] = expf(la);
   }
-  for (int e = tid; e < kC * (D / 8); e += 256) {
-    const int sr = e / (D / 8), i0 = (e % (D / 8)) * 8;
-    bf16x8 hi, lo;
-    frag8(Kb + (size_t)sr * CD + i0, sr < L, hi, lo);
+  constexpr int PER = kC * (D / 8) / 256;
+  bf16x8 kth[PER], ktl[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int e = tid + 256 * m, sr = e / (D / 8), i0 = (e % (D / 8)) * 8;
+    frag8(Kb + (size_t)min(sr, L - 1) * CD + i0, kth[m], ktl[m]);
+  }
+  // wave w owns row block w of Q K^T -> M and of K K^T -> Abar
+  const int ti = wave;
+  bf16x8 qh[KS], ql[KS], kh[4][KS], kl[4][KS];
+  {
+    const TY *qrow = Qb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) frag8(qrow + 32 * ks, qh[ks], ql[ks]);
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      const TY *krow = Kb + (size_t)min(16 * tj + lr, L - 1) * CD + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) frag8(krow + 32 * ks, kh[tj][ks], kl[tj][ks]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {  // rows past the chunk end are zero (E must see exact zeros)
+    const int e = tid + 256 * m, sr = e / (D / 8), i0 = (e % (D / 8)) * 8;
+    const bool live = sr < L;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      s_Kt[0][i0 + u][sr] = hi[u];
-      if (SP) s_Kt[NP - 1][i0 + u][sr] = lo[u];
+      s_Kt[0][i0 + u][sr] = live ? kth[m][u] : (bf16)0.0f;
+      if (SP) s_Kt[NP - 1][i0 + u][sr] = live ? ktl[m][u] : (bf16)0.0f;
     }
   }
   __syncthreads();
 
-  // ---- B: K K^T -> Abar (strictly lower), Q K^T -> M (lower incl. diagonal) ----
-#pragma unroll 1
-  for (int m = 0; m < 8; ++m) {
-    const int idx = wave + 4 * m;
-    const int which = idx >> 4, ti = (idx >> 2) & 3, tj = idx & 3;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- B: Q K^T and K K^T for row block ti ----
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) {
+    floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti) {
-      const TY *Arow = (which ? Qb : Kb) + (size_t)(16 * ti + lr) * CD + 8 * lg;
-      const TY *Brow = Kb + (size_t)(16 * tj + lr) * CD + 8 * lg;
-      const bool va = 16 * ti + lr < L, vb = 16 * tj + lr < L;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 ah, al, bh, bl;
-        frag8(Arow + 32 * ks, va, ah, al);
-        frag8(Brow + 32 * ks, vb, bh, bl);
-        acc = mma<SP, SP>(acc, ah, al, bh, bl);
+        aq = mma<SP, SP>(aq, qh[ks], ql[ks], kh[tj][ks], kl[tj][ks]);
+        ak = mma<SP, SP>(ak, kh[ti][ks], kl[ti][ks], kh[tj][ks], kl[tj][ks]);
       }
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = 16 * ti + 4 * lg + rr, c = 16 * tj + lr;
       const float dec = expf(s_gam[r] - s_gam[c]);
-      if (which == 0) {
-        s_A[r][c] = (c < r) ? s_bb[r] * dec * acc[rr] : 0.0f;
-      } else {
-        const float v = (c <= r) ? dec * acc[rr] : 0.0f;
-        bf16 hi, lo;
-        split_bf16(v, hi, lo);
-        s_M[0][r][c] = hi;
-        s_M[1][r][c] = lo;
-      }
+      s_A[r][c] = (c < r) ? s_bb[r] * dec * ak[rr] : 0.0f;
+      const float v = (c <= r) ? dec * aq[rr] : 0.0f;
+      bf16 hi, lo;
+      split_bf16(v, hi, lo);
+      s_M[0][r][c] = hi;
+      s_M[1][r][c] = lo;
     }
   }
   __syncthreads();
 
-  // ---- C: T = (I + Abar)^-1 diag(b), blocks of 16 ----
-  if (lane < 16) {  // wave w inverts diagonal block w, lane = column
-    const int bk = wave, c = lane;
+  // ---- C: L^-1 for L = I + Abar (unit lower triangular), fp32 ----
+  // Level 1: the four 16x16 diagonal blocks by substitution (wave 0: lane =
+  // block * 16 + column); the other waves clear the upper blocks.
+  if (wave == 0) {
+    const int bk = lane / 16, c = lane % 16;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -292,54 +329,66 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       for (int m = 0; m < r; ++m) acc -= s_A[16 * bk + r][16 * bk + m] * x[m];
       x[r] = acc;
     }
-    const float bc = s_bb[16 * bk + c];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s_Li[bk][r][c] = x[r];
-      s_T[16 * bk + r][16 * bk + c] = x[r] * bc;
+    for (int r = 0; r < 16; ++r) s_L[16 * bk + r][16 * bk + c] = x[r];
+  } else {
+    for (int e = tid - kWave; e < kC * kC; e += 256 - kWave) {
+      const int r = e / kC, c = e % kC;
+      if ((c >> 4) > (r >> 4)) s_L[r][c] = 0.0f;
     }
-  }
-  for (int e = tid; e < kC * kC; e += 256) {
-    const int r = e / kC, c = e % kC;
-    if ((c >> 4) > (r >> 4)) s_T[r][c] = 0.0f;
   }
   __syncthreads();
-#pragma unroll 1
-  for (int bi = 1; bi < 4; ++bi) {
-    for (int e = tid; e < bi * 256; e += 256) {
-      const int bj = e >> 8, r = (e >> 4) & 15, c = e & 15;
-      float acc = 0.0f;
-      for (int bk = bj; bk < bi; ++bk) {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) acc += s_A[16 * bi + r][16 * bk + m] * s_T[16 * bk + m][16 * bj + c];
-      }
-      s_P[bj][r][c] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < bi * 256; e += 256) {
-      const int bj = e >> 8, r = (e >> 4) & 15, c = e & 15;
-      float acc = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) acc += s_Li[bi][r][m] * s_P[bj][m][c];
-      s_T[16 * bi + r][16 * bj + c] = -acc;
-    }
-    __syncthreads();
+  // Level 2: [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1] on the two 32x32 diagonal
+  // blocks (wave 0: rows 0..31, wave 1: rows 32..63).
+  if (wave < 2) {
+    const int o = 32 * wave;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm16_f32(&s_A[o + 16][o], LF, &s_L[o][o], LF, acc, lr, lg);  // C A^-1
+    store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
   }
+  __syncthreads();
+  if (wave < 2) {
+    const int o = 32 * wave;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm16_f32(&s_L[o + 16][o + 16], LF, &s_Y[wave][0][0], 17, acc, lr, lg);  // B^-1 (C A^-1)
+    store_tile(&s_L[o + 16][o], LF, acc, -1.0f, lr, lg);
+  }
+  __syncthreads();
+  // Level 3: the same identity with 32x32 blocks; wave w owns output tile (w/2, w%2).
+  {
+    const int yi = wave >> 1, yj = wave & 1;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // Y = C A^-1, C = Abar[32:64, 0:32], A^-1 = L^-1[0:32, 0:32] (lower: k >= yj)
+    for (int k = yj; k < 2; ++k) acc = mm16_f32(&s_A[32 + 16 * yi][16 * k], LF, &s_L[16 * k][16 * yj], LF, acc, lr, lg);
+    store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
+  }
+  __syncthreads();
+  {
+    const int xi = wave >> 1, xj = wave & 1;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    // X = -B^-1 Y, B^-1 = L^-1[32:64, 32:64] (lower: k <= xi)
+    for (int k = 0; k <= xi; ++k)
+      acc = mm16_f32(&s_L[32 + 16 * xi][32 + 16 * k], LF, &s_Y[2 * k + xj][0][0], 17, acc, lr, lg);
+    store_tile(&s_L[32 + 16 * xi][16 * xj], LF, acc, -1.0f, lr, lg);
+  }
+  __syncthreads();
 
-  // ---- D: MT = M T and E = K^T diag(D) T on MFMA; wave w owns rows j of T^T ----
+  // ---- D: T = L^-1 diag(b); MT = M T and E = K^T diag(D) T on MFMA ----
+  // Wave w owns rows j in [16w, 16w + 16) of T^T; its A operands are columns of T.
   const int jrow = 16 * wave + lr;
+  const float bj = s_bb[jrow];
   bf16x8 th[2], tl[2], dh[2], dl[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int s = 8 * lg + 32 * ks + e;
-      const float tv = s_T[s][jrow];
+      const int sr = 8 * lg + 32 * ks + e;
+      const float tv = s_L[sr][jrow] * bj;
       bf16 hi, lo;
       split_bf16(tv, hi, lo);
       th[ks][e] = hi;
       tl[ks][e] = lo;
-      split_bf16(s_dec[s] * tv, hi, lo);
+      split_bf16(s_dec[sr] * tv, hi, lo);
       dh[ks][e] = hi;
       dl[ks][e] = lo;
     }
@@ -360,42 +409,53 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   }
   // E^T[j][i] = sum_s D_s T[s][j] K[s][i]; lane holds column i, rows j..j+3 -> E[i][j..j+3]
 #pragma unroll
-  for (int ti = 0; ti < NTI; ++ti) {
+  for (int tix = 0; tix < NTI; ++tix) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 kh = *reinterpret_cast<const bf16x8 *>(&s_Kt[0][16 * ti + lr][8 * lg + 32 * ks]);
-      const bf16x8 kl = SP ? *reinterpret_cast<const bf16x8 *>(&s_Kt[NP - 1][16 * ti + lr][8 * lg + 32 * ks])
-                           : zero8();
-      acc = mma<true, SP>(acc, dh[ks], dl[ks], kh, kl);
+      const bf16x8 khh = *reinterpret_cast<const bf16x8 *>(&s_Kt[0][16 * tix + lr][8 * lg + 32 * ks]);
+      const bf16x8 kll = SP ? *reinterpret_cast<const bf16x8 *>(&s_Kt[NP - 1][16 * tix + lr][8 * lg + 32 * ks])
+                            : zero8();
+      acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
     }
-    const int i = 16 * ti + lr, j0 = 16 * wave + 4 * lg;
+    const int i = 16 * tix + lr, j0 = 16 * wave + 4 * lg;
     const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
     store_split4(E_hi + i * kC + j0, E_lo + i * kC + j0, v);
   }
 }
 
 // ---- 3. the serial pass over chunks -------------------------------------------
+// 512 threads per (sequence, value head, 32-column block of d_v).  Waves 0-3 are
+// "K-waves": wave w computes P = K h for token rows 16w..16w+15 and writes
+// X = V - Gam P.  Waves 4-7 are "Q-waves": R = Q h for the same rows, then
+// O = Gam R + MT X.  Every wave w < d/16 owns state rows 16w..16w+15 of the block
+// (two 16x16 MFMA accumulators) and applies h <- Gam_63 h + E X to them.  Each
+// wave's A operands (K or Q rows, E rows, MT rows) serve two 16-column tiles from
+// registers, so the operands of a head are read by d/32 workgroups instead of d/16,
+// and the two tiles give every MFMA chain an independent partner.
+constexpr int kCols = 32;  // state columns per workgroup
+
 template <int D, typename TY>
 struct ChunkOps {
   static constexpr int KS = D / 32;
   static constexpr int NRT = D / 16;
-  static constexpr int TPW = (NRT + 3) / 4;
-  bf16x8 kh[KS], kl[KS], qh[KS], ql[KS];   // K, Q rows of this wave's 16 tokens
-  bf16x8 eh[TPW][2], el[TPW][2];          // E rows of this wave's state tiles
-  bf16x8 mh[2], ml[2];                    // MT rows of this wave's 16 tokens
-  float gam[4], v[4], gC;
+  bf16x8 ah[KS], al[KS];      // K rows (K-waves) or Q rows (Q-waves) of the wave's 16 tokens
+  bf16x8 eh[2], el[2];        // E rows of the wave's state tile
+  bf16x8 mh[2], ml[2];        // MT rows of the wave's 16 tokens (Q-waves)
+  float gam[4], v[2][4], gC;
   int t0, L;
 };
 
 template <int D, typename TY>
-__device__ __forceinline__ void load_chunk(ChunkOps<D, TY> &f, const PrefillLaunch &p, const Tables &tb,
-                                           const char *units, int cidx, int h, int g, int cb, int wave,
-                                           int lr, int lg) {
+__device__ __forceinline__ void load_chunk(ChunkOps<D, TY> &f, const PrefillLaunch &p, const char *units,
+                                           int cidx, int t0, int L, int h, int g, int cb, int wave, int lr,
+                                           int lg) {
   using F = ChunkOps<D, TY>;
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, CD = p.geo.conv_dim;
-  f.t0 = tb.chunk_start[cidx];
-  f.L = tb.chunk_len[cidx];
+  const bool qwave = wave >= 4;
+  const int rb = wave & 3;
+  f.t0 = t0;
+  f.L = L;
   const char *unit = units + ((size_t)cidx * Hv + h) * unit_bytes(D);
   const bf16 *E_hi = reinterpret_cast<const bf16 *>(unit);
   const bf16 *E_lo = E_hi + D * kC;
@@ -403,151 +463,179 @@ __device__ __forceinline__ void load_chunk(ChunkOps<D, TY> &f, const PrefillLaun
   const bf16 *MT_lo = MT_hi + kC * kC;
   const float *Gam = reinterpret_cast<const float *>(MT_lo + kC * kC);
   const TY *y = static_cast<const TY *>(p.y);
-  const int srow = 16 * wave + lr;
-  const bool valid = srow < f.L;
-  const TY *qrow = y + (size_t)(f.t0 + (valid ? srow : 0)) * CD + (size_t)g * D + 8 * lg;
-  const TY *krow = qrow + (size_t)Hk * D;
+  // rows past the chunk end are clamped into it: they only meet zero columns of
+  // E and MT, and their outputs are not stored
+  const TY *arow = y + (size_t)(t0 + min(16 * rb + lr, L - 1)) * CD + (size_t)((qwave ? 0 : Hk) + g) * D + 8 * lg;
 #pragma unroll
-  for (int ks = 0; ks < F::KS; ++ks) {
-    frag8(krow + 32 * ks, valid, f.kh[ks], f.kl[ks]);
-    frag8(qrow + 32 * ks, valid, f.qh[ks], f.ql[ks]);
-  }
-#pragma unroll
-  for (int k = 0; k < F::TPW; ++k) {
-    const int rt = wave + 4 * k;
+  for (int ks = 0; ks < F::KS; ++ks) frag8(arow + 32 * ks, f.ah[ks], f.al[ks]);
+  if (wave < F::NRT) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      if (rt < F::NRT) {
-        f.eh[k][ks] = *reinterpret_cast<const bf16x8 *>(E_hi + (16 * rt + lr) * kC + 8 * lg + 32 * ks);
-        f.el[k][ks] = *reinterpret_cast<const bf16x8 *>(E_lo + (16 * rt + lr) * kC + 8 * lg + 32 * ks);
-      } else {
-        f.eh[k][ks] = zero8();
-        f.el[k][ks] = zero8();
-      }
+      f.eh[ks] = *reinterpret_cast<const bf16x8 *>(E_hi + (16 * wave + lr) * kC + 8 * lg + 32 * ks);
+      f.el[ks] = *reinterpret_cast<const bf16x8 *>(E_lo + (16 * wave + lr) * kC + 8 * lg + 32 * ks);
+    }
+  }
+  if (qwave) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f.mh[ks] = *reinterpret_cast<const bf16x8 *>(MT_hi + (16 * rb + lr) * kC + 8 * lg + 32 * ks);
+      f.ml[ks] = *reinterpret_cast<const bf16x8 *>(MT_lo + (16 * rb + lr) * kC + 8 * lg + 32 * ks);
     }
   }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    f.mh[ks] = *reinterpret_cast<const bf16x8 *>(MT_hi + (16 * wave + lr) * kC + 8 * lg + 32 * ks);
-    f.ml[ks] = *reinterpret_cast<const bf16x8 *>(MT_lo + (16 * wave + lr) * kC + 8 * lg + 32 * ks);
-  }
-#pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int s = 16 * wave + 4 * lg + rr;
-    f.gam[rr] = Gam[s];
-    f.v[rr] = (s < f.L) ? ld(y, (size_t)(f.t0 + s) * CD + (size_t)2 * Hk * D + (size_t)h * D + 16 * cb + lr)
-                        : 0.0f;
+    const int srow = 16 * rb + 4 * lg + rr;
+    f.gam[rr] = Gam[srow];
+    if (!qwave) {
+      const size_t vb = (size_t)(t0 + min(srow, L - 1)) * CD + (size_t)2 * Hk * D + (size_t)h * D + kCols * cb + lr;
+      f.v[0][rr] = ld(y, vb);
+      f.v[1][rr] = ld(y, vb + 16);
+    }
   }
   f.gC = Gam[kC - 1];
 }
 
 template <int D, typename TY, typename TO>
-__global__ __launch_bounds__(256) void spine_kernel(PrefillLaunch p, Tables tb, const char *units) {
-  constexpr bool SP = std::is_same<TY, float>::value;
+__device__ __forceinline__ void spine_step(const ChunkOps<D, TY> &cur, floatx4 (&hacc)[2],
+                                           bf16 (*s_hT)[kCols][D + 8], bf16 (*s_XT)[kCols][kLP], TO *o,
+                                           float scale, int Hv, int h, int cb, int wave, int lr, int lg) {
   using F = ChunkOps<D, TY>;
-  constexpr int NCB = D / 16;
+  constexpr bool SP = std::is_same<TY, float>::value;
+  const bool qwave = wave >= 4;
+  const int rb = wave & 3;
+  // stage 1: P = K h (K-waves) or R = Q h (Q-waves) for token rows 16 rb .., two
+  // column tiles, accumulators split by k-step parity for independent chains
+  floatx4 acc[2][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) acc[ct][e] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < F::KS; ++ks) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&s_hT[0][16 * ct + lr][8 * lg + 32 * ks]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&s_hT[1][16 * ct + lr][8 * lg + 32 * ks]);
+      acc[ct][ks & 1] = mma<SP, true>(acc[ct][ks & 1], cur.ah[ks], cur.al[ks], bh, bl);
+    }
+  }
+  floatx4 O[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    if (!qwave) {
+      float X[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) X[rr] = cur.v[ct][rr] - cur.gam[rr] * (acc[ct][0][rr] + acc[ct][1][rr]);
+      store_split4(&s_XT[0][16 * ct + lr][16 * rb + 4 * lg], &s_XT[1][16 * ct + lr][16 * rb + 4 * lg], X);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) O[ct][rr] = cur.gam[rr] * (acc[ct][0][rr] + acc[ct][1][rr]);
+    }
+  }
+  __syncthreads();
+
+  // stage 2: h <- Gam_63 h + E X (state tile owners), O = Gam R + MT X (Q-waves)
+  bf16x8 xh[2][2], xl[2][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      xh[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[0][16 * ct + lr][8 * lg + 32 * ks]);
+      xl[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[1][16 * ct + lr][8 * lg + 32 * ks]);
+    }
+  if (wave < F::NRT) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) hacc[ct][rr] *= cur.gC;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        hacc[ct] = mma<true, true>(hacc[ct], cur.eh[ks], cur.el[ks], xh[ct][ks], xl[ct][ks]);
+      const float v[4] = {hacc[ct][0], hacc[ct][1], hacc[ct][2], hacc[ct][3]};
+      store_split4(&s_hT[0][16 * ct + lr][16 * wave + 4 * lg], &s_hT[1][16 * ct + lr][16 * wave + 4 * lg], v);
+    }
+  }
+  if (qwave) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) O[ct] = mma<true, true>(O[ct], cur.mh[ks], cur.ml[ks], xh[ct][ks], xl[ct][ks]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int srow = 16 * rb + 4 * lg + rr;
+        if (srow < cur.L)
+          st(o, (size_t)(cur.t0 + srow) * Hv * D + (size_t)h * D + kCols * cb + 16 * ct + lr, scale * O[ct][rr]);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int D, typename TY, typename TO>
+__global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, const char *units) {
+  using F = ChunkOps<D, TY>;
+  constexpr int NCB = D / kCols;
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk;
-  // Each group of 64 consecutive workgroups is dispatched round-robin over the 8
-  // XCDs; remap so that every XCD receives 8 consecutive logical blocks (the
-  // column blocks of one head when d = 128), keeping the longest-first order.
+  // Consecutive workgroups are dispatched round-robin over the 8 XCDs; within
+  // each group of 8 * NCB, remap so that one XCD receives the NCB column blocks of
+  // one head (they share its operands through one L2), keeping the
+  // longest-sequence-first order between groups.
   int b = blockIdx.x;
-  const int nb = gridDim.x;
-  if (b < nb - nb % 64) b = (b & ~63) | ((b & 7) << 3) | ((b & 63) >> 3);
+  const int nb = gridDim.x, grp = 8 * NCB;
+  if (b < nb - nb % grp) {
+    const int r = b % grp;
+    b = (b - r) + (r % 8) * NCB + r / 8;
+  }
   const int cb = b % NCB, hq = b / NCB, h = hq % Hv, q = hq / Hv;
   const int seq = tb.order[q];
   const int c_first = tb.seq_chunk0[seq], nch = tb.seq_chunk0[seq + 1] - c_first;
   if (nch == 0) return;  // zero-length sequence: state unchanged
+  // chunk c of the sequence starts at row seq_t0 + 64 c (no table loads in the loop)
+  const int seq_t0 = p.cu[seq], seq_len = p.cu[seq + 1] - seq_t0;
   const int g = h / G;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
+  const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
-  __shared__ __align__(16) bf16 s_hT[2][16][D + 8];   // state block, transposed [j][i], hi/lo
-  __shared__ __align__(16) bf16 s_XT[2][16][kLP];     // X block, transposed [j][s], hi/lo
+  __shared__ __align__(16) bf16 s_hT[2][kCols][D + 8];   // state block, transposed [j][i], hi/lo
+  __shared__ __align__(16) bf16 s_XT[2][kCols][kLP];     // X block, transposed [j][s], hi/lo
 
-  float *hs = p.h_state[seq] + (size_t)h * D * D;
-  floatx4 hacc[F::TPW];
+  float *hs = p.h_state[seq] + (size_t)h * D * D + kCols * cb;
+  floatx4 hacc[2];
 #pragma unroll
-  for (int k = 0; k < F::TPW; ++k) {
-    const int rt = wave + 4 * k;
+  for (int ct = 0; ct < 2; ++ct) {
+    hacc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (wave < F::NRT) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      hacc[k][rr] = (rt < F::NRT) ? hs[(size_t)(16 * rt + 4 * lg + rr) * D + 16 * cb + lr] : 0.0f;
-    if (rt < F::NRT) {
-      const float v[4] = {hacc[k][0], hacc[k][1], hacc[k][2], hacc[k][3]};
-      store_split4(&s_hT[0][lr][16 * rt + 4 * lg], &s_hT[1][lr][16 * rt + 4 * lg], v);
+      for (int rr = 0; rr < 4; ++rr) hacc[ct][rr] = hs[(size_t)(16 * wave + 4 * lg + rr) * D + 16 * ct + lr];
+      const float v[4] = {hacc[ct][0], hacc[ct][1], hacc[ct][2], hacc[ct][3]};
+      store_split4(&s_hT[0][16 * ct + lr][16 * wave + 4 * lg], &s_hT[1][16 * ct + lr][16 * wave + 4 * lg], v);
     }
   }
   __syncthreads();
 
   TO *o = static_cast<TO *>(p.o);
-  F cur;
-  load_chunk<D, TY>(cur, p, tb, units, c_first, h, g, cb, wave, lr, lg);
+  // Two operand buffers in ping-pong: the loads for chunk c+1 are in flight while
+  // chunk c computes, and no register copy forces them to land early.
+  F bufA, bufB;
+  auto chunk_load = [&](F &f, int c) {
+    const int cc = min(c, nch - 1);  // past the end: re-load the last chunk, unused
+    load_chunk<D, TY>(f, p, units, c_first + cc, seq_t0 + kC * cc, min(kC, seq_len - kC * cc), h, g, cb, wave,
+                      lr, lg);
+  };
+  chunk_load(bufA, 0);
 #pragma unroll 1
-  for (int c = 0; c < nch; ++c) {
-    F nxt;
-    if (c + 1 < nch) load_chunk<D, TY>(nxt, p, tb, units, c_first + c + 1, h, g, cb, wave, lr, lg);
-
-    // stage 1: rows s of this wave -- P = K h, R = Q h, X = V - Gam P
-    floatx4 P = {0.f, 0.f, 0.f, 0.f}, R = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks) {
-      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&s_hT[0][lr][8 * lg + 32 * ks]);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&s_hT[1][lr][8 * lg + 32 * ks]);
-      P = mma<SP, true>(P, cur.kh[ks], cur.kl[ks], bh, bl);
-      R = mma<SP, true>(R, cur.qh[ks], cur.ql[ks], bh, bl);
-    }
-    float X[4];
-    floatx4 O;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      X[rr] = cur.v[rr] - cur.gam[rr] * P[rr];
-      O[rr] = cur.gam[rr] * R[rr];
-    }
-    store_split4(&s_XT[0][lr][16 * wave + 4 * lg], &s_XT[1][lr][16 * wave + 4 * lg], X);
-    __syncthreads();
-
-    // stage 2: h <- Gam_63 h + E X,  O = Gam Q h + MT X
-    bf16x8 xh[2], xl[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      xh[ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[0][lr][8 * lg + 32 * ks]);
-      xl[ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[1][lr][8 * lg + 32 * ks]);
-    }
-#pragma unroll
-    for (int k = 0; k < F::TPW; ++k) {
-      const int rt = wave + 4 * k;
-      if (rt < F::NRT) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) hacc[k][rr] *= cur.gC;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) hacc[k] = mma<true, true>(hacc[k], cur.eh[k][ks], cur.el[k][ks], xh[ks], xl[ks]);
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) O = mma<true, true>(O, cur.mh[ks], cur.ml[ks], xh[ks], xl[ks]);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int s = 16 * wave + 4 * lg + rr;
-      if (s < cur.L)
-        st(o, (size_t)(cur.t0 + s) * Hv * D + (size_t)h * D + 16 * cb + lr, p.scale * O[rr]);
-    }
-#pragma unroll
-    for (int k = 0; k < F::TPW; ++k) {
-      const int rt = wave + 4 * k;
-      if (rt < F::NRT) {
-        const float v[4] = {hacc[k][0], hacc[k][1], hacc[k][2], hacc[k][3]};
-        store_split4(&s_hT[0][lr][16 * rt + 4 * lg], &s_hT[1][lr][16 * rt + 4 * lg], v);
-      }
-    }
-    __syncthreads();
-    cur = nxt;
+  for (int c = 0; c < nch; c += 2) {
+    chunk_load(bufB, c + 1);
+    spine_step<D, TY, TO>(bufA, hacc, s_hT, s_XT, o, p.scale, Hv, h, cb, wave, lr, lg);
+    if (c + 1 >= nch) break;
+    chunk_load(bufA, c + 2);
+    spine_step<D, TY, TO>(bufB, hacc, s_hT, s_XT, o, p.scale, Hv, h, cb, wave, lr, lg);
   }
+  if (wave < F::NRT) {
 #pragma unroll
-  for (int k = 0; k < F::TPW; ++k) {
-    const int rt = wave + 4 * k;
-    if (rt < F::NRT) {
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) hs[(size_t)(16 * rt + 4 * lg + rr) * D + 16 * cb + lr] = hacc[k][rr];
-    }
+      for (int rr = 0; rr < 4; ++rr) hs[(size_t)(16 * wave + 4 * lg + rr) * D + 16 * ct + lr] = hacc[ct][rr];
   }
 }
 
@@ -563,7 +651,7 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
   hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hv)), dim3(256), 0, stream, p, tb, units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((spine_kernel<D, TY, TO>), dim3((unsigned)(p.n * p.geo.Hv * (D / 16))), dim3(256), 0,
+  hipLaunchKernelGGL((spine_kernel<D, TY, TO>), dim3((unsigned)(p.n * p.geo.Hv * (D / kCols))), dim3(512), 0,
                      stream, p, tb, static_cast<const char *>(units));
   return hipGetLastError();
 }

@@ -47,17 +47,35 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   __shared__ float4 s_red[2][G][4][CQ][2];
 
   const int Hk = p.geo.Hk, Hv = p.geo.Hv, K = p.geo.K, C = p.geo.conv_dim;
-  const int i = blockIdx.x / Hk;
-  const int g = blockIdx.x - i * Hk;
+  const int rank = blockIdx.x / Hk;
+  const int g = blockIdx.x - rank * Hk;
   const int tid = threadIdx.x;
 
-  int r0, nrows;
+  int i, r0, nrows;
   if (MAXR == 1) {
+    i = rank;
     r0 = i;
     nrows = 1;
   } else {
-    r0 = p.cu[i];
-    nrows = p.cu[i + 1] - r0;
+    // verify: workgroups take sequences longest draft first, so the long ones
+    // do not trail at the end of the grid (ranks of the <= 128 lengths, ties by index)
+    __shared__ int s_cu[kTableSeqs + 1];
+    __shared__ int s_seq;
+    for (int t = tid; t <= p.n; t += NT) s_cu[t] = p.cu[t];
+    __syncthreads();
+    for (int t = tid; t < p.n; t += NT) {
+      const int kt = s_cu[t + 1] - s_cu[t];
+      int rk = 0;
+      for (int s2 = 0; s2 < p.n; ++s2) {
+        const int k2 = s_cu[s2 + 1] - s_cu[s2];
+        rk += (k2 > kt) || (k2 == kt && s2 < t);
+      }
+      if (rk == rank) s_seq = t;
+    }
+    __syncthreads();
+    i = s_seq;
+    r0 = s_cu[i];
+    nrows = s_cu[i + 1] - r0;
     nrows = nrows < 0 ? 0 : (nrows > MAXR ? MAXR : nrows);
   }
   if (nrows == 0) return;  // uniform over the block
@@ -214,34 +232,38 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
 }
 
 // Commit: copy the state after the last accepted row into table 0 and advance the
-// conv state over the accepted rows.  blockIdx.y < nblk_state: state copy slice;
-// otherwise conv-state channels.
+// conv state over the accepted rows.  blockIdx.y < kCommitSplit: one eighth of the
+// state copy, 8 loads in flight per thread; otherwise conv-state channels.
+constexpr int kCommitSplit = 8;
+
 template <typename TE>
-__global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int nblk_state, int64_t n4) {
+__global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4) {
   const int i = blockIdx.x;
   const int k = p.cu[i + 1] - p.cu[i];
   const int na = p.n_accepted[i];
   if (na < 1 || na > k) return;  // outside the caller's contract: sequence untouched
-  if ((int)blockIdx.y < nblk_state) {
+  if ((int)blockIdx.y < kCommitSplit) {
     if (na == k) return;  // table 0 already holds the last state
     const float4 *src = reinterpret_cast<const float4 *>(p.tables[na * kTableSeqs + i]);
     float4 *dst = reinterpret_cast<float4 *>(p.tables[i]);
-    const int64_t per_blk = 256 * 8;
-    const int64_t base = (int64_t)blockIdx.y * per_blk + threadIdx.x;
-    float4 v[8];
+    const int64_t per = (n4 + kCommitSplit - 1) / kCommitSplit;
+    const int64_t beg = (int64_t)blockIdx.y * per, end = min(n4, beg + per);
+    for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += 256 * 8) {
+      float4 v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t idx = base + (int64_t)e * 256;
-      if (idx < n4) v[e] = src[idx];
-    }
+      for (int u = 0; u < 8; ++u) {
+        const int64_t idx = i0 + (int64_t)u * 256;
+        if (idx < end) v[u] = src[idx];
+      }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t idx = base + (int64_t)e * 256;
-      if (idx < n4) dst[idx] = v[e];
+      for (int u = 0; u < 8; ++u) {
+        const int64_t idx = i0 + (int64_t)u * 256;
+        if (idx < end) dst[idx] = v[u];
+      }
     }
   } else {
     const int C = p.geo.conv_dim, R = p.geo.K - 1;
-    const int c = ((int)blockIdx.y - nblk_state) * 256 + threadIdx.x;
+    const int c = ((int)blockIdx.y - kCommitSplit) * 256 + threadIdx.x;
     if (c >= C) return;
     TE *ring = static_cast<TE *>(p.conv_state[i]);
     const TE *x = static_cast<const TE *>(p.x) + (size_t)p.cu[i] * C;
@@ -305,13 +327,12 @@ hipError_t launch_recurrent(const RecurrentLaunch &p, hipStream_t stream) {
 hipError_t launch_commit(const CommitLaunch &p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;
   const int64_t n4 = (int64_t)p.geo.Hv * p.geo.D * p.geo.D / 4;
-  const int nblk_state = (int)((n4 + 256 * 8 - 1) / (256 * 8));
   const int nblk_ring = (p.geo.conv_dim + 255) / 256;
-  const dim3 grid(p.n, nblk_state + nblk_ring), block(256);
+  const dim3 grid(p.n, kCommitSplit + nblk_ring), block(256);
   if (p.geo.act_bf16)
-    hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, nblk_state, n4);
+    hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, n4);
   else
-    hipLaunchKernelGGL((commit_kernel<float>), grid, block, 0, stream, p, nblk_state, n4);
+    hipLaunchKernelGGL((commit_kernel<float>), grid, block, 0, stream, p, n4);
   return hipGetLastError();
 }
 
