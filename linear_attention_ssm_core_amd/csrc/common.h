@@ -12,6 +12,19 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Global-memory pointers.  A pointer read from memory (an array of per-sequence
+// state pointers, say) is not known to the compiler to address global memory, so
+// its accesses become FLAT instructions, which also count against the LDS/scalar
+// counter and make the compiler wait for every outstanding memory operation at
+// the next wait.  Casting to the global address space keeps them vector-memory
+// operations.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T *;
+template <typename T>
+__device__ __forceinline__ gptr<T> to_global(T *p) {
+  return (gptr<T>)p;
+}
+
 // ---- scalar element access for the two activation dtypes --------------------
 __device__ __forceinline__ float ld(const float *p, size_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const bf16 *p, size_t i) { return (float)p[i]; }

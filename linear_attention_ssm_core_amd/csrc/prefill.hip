@@ -393,6 +393,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       dl[ks][e] = lo;
     }
   }
+  // The lane's results below are X[r0 + lr][16 wave + 4 lg + r], r = 0..3 (X = MT or E,
+  // r0 the tile's first row): k-offset 16 (wave & 1) + 4 lg + r within k-step wave / 2,
+  // i.e. fragment lane fl, elements fe .. fe + 3.
+  const int fl = lr + 16 * (2 * (wave & 1) + (lg >> 1)), fe = 4 * (lg & 1);
   // MT^T[j][t] = sum_s T[s][j] M[t][s]; lane holds column t, rows j..j+3 -> MT[t][j..j+3]
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
@@ -403,9 +407,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       const bf16x8 ml = *reinterpret_cast<const bf16x8 *>(&s_M[1][16 * tt + lr][8 * lg + 32 * ks]);
       acc = mma<true, true>(acc, th[ks], tl[ks], mh, ml);
     }
-    const int t = 16 * tt + lr, j0 = 16 * wave + 4 * lg;
     const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    store_split4(MT_hi + t * kC + j0, MT_lo + t * kC + j0, v);
+    const int fo = frag_off(tt, wave >> 1, 2, fl) + fe;
+    store_split4(MT_hi + fo, MT_lo + fo, v);
   }
   // E^T[j][i] = sum_s D_s T[s][j] K[s][i]; lane holds column i, rows j..j+3 -> E[i][j..j+3]
 #pragma unroll
@@ -418,164 +422,102 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
                             : zero8();
       acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
     }
-    const int i = 16 * tix + lr, j0 = 16 * wave + 4 * lg;
     const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    store_split4(E_hi + i * kC + j0, E_lo + i * kC + j0, v);
+    const int fo = frag_off(tix, wave >> 1, 2, fl) + fe;
+    store_split4(E_hi + fo, E_lo + fo, v);
   }
 }
 
 // ---- 3. the serial pass over chunks -------------------------------------------
-// 512 threads per (sequence, value head, 32-column block of d_v).  Waves 0-3 are
-// "K-waves": wave w computes P = K h for token rows 16w..16w+15 and writes
-// X = V - Gam P.  Waves 4-7 are "Q-waves": R = Q h for the same rows, then
-// O = Gam R + MT X.  Every wave w < d/16 owns state rows 16w..16w+15 of the block
-// (two 16x16 MFMA accumulators) and applies h <- Gam_63 h + E X to them.  Each
-// wave's A operands (K or Q rows, E rows, MT rows) serve two 16-column tiles from
-// registers, so the operands of a head are read by d/32 workgroups instead of d/16,
-// and the two tiles give every MFMA chain an independent partner.
+// 512 threads per (sequence, value head, 32-column block of d_v).  Columns of h
+// evolve independently, so a d_v-wide state splits over d_v / 32 workgroups.
+//   waves 0-3 ("row waves"): token rows 32 (w & 1) .. +31 of K (w < 2) or Q (w >= 2),
+//       both 16-column tiles.  Stage 1: P = K h -> X = V - Gam P -> LDS (K), or
+//       R^T = h^T Q^T (Q).  Stage 2 (Q): O^T = Gam R^T + X^T MT^T, stored.
+//   waves 4-7 ("owners"): state rows 32 (w - 4) .. +31 of the block live in their
+//       MFMA accumulators.  Stage 2: h <- Gam_63 h + E X, copied as bf16 hi/lo h^T
+//       to LDS for the next stage 1.
+// One barrier after each stage.  Each wave loads exactly the operands it consumes
+// (84 KiB per chunk and workgroup at d = 128, nothing read twice).  The per-CU
+// vector-memory path moves about 64 B per clock, so these loads take as long as
+// the arithmetic; they are issued by waves that have nothing else to do at that
+// moment, so that a full queue stalls nobody on the critical path: owners fetch
+// the next chunk's E during stage 1 (double-buffered; chunk parity picks the half
+// at compile time, so no register copy forces a load to land early), K-row waves
+// fetch the next K rows, V and Gam during stage 2, Q-row waves the next Q rows and
+// MT once their O products are in flight.  O is formed transposed,
+// so a lane holds four consecutive columns of one token row and stores them at once.
 constexpr int kCols = 32;  // state columns per workgroup
 
-template <int D, typename TY>
-struct ChunkOps {
-  static constexpr int KS = D / 32;
-  static constexpr int NRT = D / 16;
-  bf16x8 ah[KS], al[KS];      // K rows (K-waves) or Q rows (Q-waves) of the wave's 16 tokens
-  bf16x8 eh[2], el[2];        // E rows of the wave's state tile
-  bf16x8 mh[2], ml[2];        // MT rows of the wave's 16 tokens (Q-waves)
-  float gam[4], v[2][4], gC;
-  int t0, L;
-};
+// Raw 16-byte register slots.  Row waves keep their K or Q rows in `sl` (bf16:
+// entry rt * KS + ks; fp32: the pair 2 (rt * KS + ks) + {0, 1}); owners keep E
+// fragments there ([parity][tile][hi k0, hi k1, lo k0, lo k1], entry 8 parity +
+// 4 tile + i).  `sx` holds V (16 values, one per 32-bit lane of entries 0-3) and
+// Gam (entries 4-5) for K-row waves, MT fragments (entries 4 rt + i) and Gam
+// (entry 8) for Q-row waves.
+typedef uint4 Slot[16];
+typedef uint4 SlotX[9];
 
-template <int D, typename TY>
-__device__ __forceinline__ void load_chunk(ChunkOps<D, TY> &f, const PrefillLaunch &p, const char *units,
-                                           int cidx, int t0, int L, int h, int g, int cb, int wave, int lr,
-                                           int lg) {
-  using F = ChunkOps<D, TY>;
-  const int Hv = p.geo.Hv, Hk = p.geo.Hk, CD = p.geo.conv_dim;
-  const bool qwave = wave >= 4;
-  const int rb = wave & 3;
-  f.t0 = t0;
-  f.L = L;
-  const char *unit = units + ((size_t)cidx * Hv + h) * unit_bytes(D);
-  const bf16 *E_hi = reinterpret_cast<const bf16 *>(unit);
-  const bf16 *E_lo = E_hi + D * kC;
-  const bf16 *MT_hi = E_lo + D * kC;
-  const bf16 *MT_lo = MT_hi + kC * kC;
-  const float *Gam = reinterpret_cast<const float *>(MT_lo + kC * kC);
-  const TY *y = static_cast<const TY *>(p.y);
-  // rows past the chunk end are clamped into it: they only meet zero columns of
-  // E and MT, and their outputs are not stored
-  const TY *arow = y + (size_t)(t0 + min(16 * rb + lr, L - 1)) * CD + (size_t)((qwave ? 0 : Hk) + g) * D + 8 * lg;
+__device__ __forceinline__ void load_row(Slot &sl, int i, const bf16 *p) {
+  sl[i] = *reinterpret_cast<const uint4 *>(p);
+}
+__device__ __forceinline__ void load_row(Slot &sl, int i, const float *p) {
+  sl[2 * i] = reinterpret_cast<const uint4 *>(p)[0];
+  sl[2 * i + 1] = reinterpret_cast<const uint4 *>(p)[1];
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
+template <typename TY>
+__device__ __forceinline__ void row_split(const Slot &sl, int i, bf16x8 &hi, bf16x8 &lo) {
+  if constexpr (std::is_same<TY, bf16>::value) {
+    hi = as_bf16x8(sl[i]);
+    lo = hi;  // unused: bf16 activations are exact
+  } else {
+    const float4 a = __builtin_bit_cast(float4, sl[2 * i]), b = __builtin_bit_cast(float4, sl[2 * i + 1]);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-  for (int ks = 0; ks < F::KS; ++ks) frag8(arow + 32 * ks, f.ah[ks], f.al[ks]);
-  if (wave < F::NRT) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f.eh[ks] = *reinterpret_cast<const bf16x8 *>(E_hi + (16 * wave + lr) * kC + 8 * lg + 32 * ks);
-      f.el[ks] = *reinterpret_cast<const bf16x8 *>(E_lo + (16 * wave + lr) * kC + 8 * lg + 32 * ks);
+    for (int e = 0; e < 8; ++e) {
+      bf16 h, l;
+      split_bf16(v[e], h, l);
+      hi[e] = h;
+      lo[e] = l;
     }
   }
-  if (qwave) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f.mh[ks] = *reinterpret_cast<const bf16x8 *>(MT_hi + (16 * rb + lr) * kC + 8 * lg + 32 * ks);
-      f.ml[ks] = *reinterpret_cast<const bf16x8 *>(MT_lo + (16 * rb + lr) * kC + 8 * lg + 32 * ks);
-    }
-  }
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int srow = 16 * rb + 4 * lg + rr;
-    f.gam[rr] = Gam[srow];
-    if (!qwave) {
-      const size_t vb = (size_t)(t0 + min(srow, L - 1)) * CD + (size_t)2 * Hk * D + (size_t)h * D + kCols * cb + lr;
-      f.v[0][rr] = ld(y, vb);
-      f.v[1][rr] = ld(y, vb + 16);
-    }
-  }
-  f.gC = Gam[kC - 1];
+}
+// One activation, loaded raw into a 32-bit register and widened at use.
+__device__ __forceinline__ uint32_t load_raw(const bf16 *p) { return *reinterpret_cast<const uint16_t *>(p); }
+__device__ __forceinline__ uint32_t load_raw(const float *p) { return *reinterpret_cast<const uint32_t *>(p); }
+template <typename TY>
+__device__ __forceinline__ float widen(uint32_t u) {
+  if constexpr (std::is_same<TY, bf16>::value) return __builtin_bit_cast(float, u << 16);
+  else return __builtin_bit_cast(float, u);
+}
+__device__ __forceinline__ uint32_t &lane32(uint4 &u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+__device__ __forceinline__ uint32_t lane32(const uint4 &u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
 }
 
-template <int D, typename TY, typename TO>
-__device__ __forceinline__ void spine_step(const ChunkOps<D, TY> &cur, floatx4 (&hacc)[2],
-                                           bf16 (*s_hT)[kCols][D + 8], bf16 (*s_XT)[kCols][kLP], TO *o,
-                                           float scale, int Hv, int h, int cb, int wave, int lr, int lg) {
-  using F = ChunkOps<D, TY>;
-  constexpr bool SP = std::is_same<TY, float>::value;
-  const bool qwave = wave >= 4;
-  const int rb = wave & 3;
-  // stage 1: P = K h (K-waves) or R = Q h (Q-waves) for token rows 16 rb .., two
-  // column tiles, accumulators split by k-step parity for independent chains
-  floatx4 acc[2][2];
+__device__ __forceinline__ void store4(float *p, const float v[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
+  union {
+    bf16 b[4];
+    uint2 u;
+  } w;
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) acc[ct][e] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < F::KS; ++ks) {
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(&s_hT[0][16 * ct + lr][8 * lg + 32 * ks]);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8 *>(&s_hT[1][16 * ct + lr][8 * lg + 32 * ks]);
-      acc[ct][ks & 1] = mma<SP, true>(acc[ct][ks & 1], cur.ah[ks], cur.al[ks], bh, bl);
-    }
-  }
-  floatx4 O[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    if (!qwave) {
-      float X[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) X[rr] = cur.v[ct][rr] - cur.gam[rr] * (acc[ct][0][rr] + acc[ct][1][rr]);
-      store_split4(&s_XT[0][16 * ct + lr][16 * rb + 4 * lg], &s_XT[1][16 * ct + lr][16 * rb + 4 * lg], X);
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) O[ct][rr] = cur.gam[rr] * (acc[ct][0][rr] + acc[ct][1][rr]);
-    }
-  }
-  __syncthreads();
-
-  // stage 2: h <- Gam_63 h + E X (state tile owners), O = Gam R + MT X (Q-waves)
-  bf16x8 xh[2][2], xl[2][2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      xh[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[0][16 * ct + lr][8 * lg + 32 * ks]);
-      xl[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[1][16 * ct + lr][8 * lg + 32 * ks]);
-    }
-  if (wave < F::NRT) {
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) hacc[ct][rr] *= cur.gC;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        hacc[ct] = mma<true, true>(hacc[ct], cur.eh[ks], cur.el[ks], xh[ct][ks], xl[ct][ks]);
-      const float v[4] = {hacc[ct][0], hacc[ct][1], hacc[ct][2], hacc[ct][3]};
-      store_split4(&s_hT[0][16 * ct + lr][16 * wave + 4 * lg], &s_hT[1][16 * ct + lr][16 * wave + 4 * lg], v);
-    }
-  }
-  if (qwave) {
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) O[ct] = mma<true, true>(O[ct], cur.mh[ks], cur.ml[ks], xh[ct][ks], xl[ct][ks]);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int srow = 16 * rb + 4 * lg + rr;
-        if (srow < cur.L)
-          st(o, (size_t)(cur.t0 + srow) * Hv * D + (size_t)h * D + kCols * cb + 16 * ct + lr, scale * O[ct][rr]);
-      }
-    }
-  }
-  __syncthreads();
+  for (int e = 0; e < 4; ++e) w.b[e] = (bf16)v[e];
+  *reinterpret_cast<uint2 *>(p) = w.u;
 }
 
 template <int D, typename TY, typename TO>
 __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, const char *units) {
-  using F = ChunkOps<D, TY>;
+  constexpr bool SP = std::is_same<TY, float>::value;
+  constexpr int KS = D / 32;
+  constexpr int NRT = D / 16;
   constexpr int NCB = D / kCols;
-  const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk;
+  const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   // Consecutive workgroups are dispatched round-robin over the 8 XCDs; within
   // each group of 8 * NCB, remap so that one XCD receives the NCB column blocks of
   // one head (they share its operands through one L2), keeping the
@@ -595,47 +537,275 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   const int g = h / G;
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const bool rowwave = wave < 4, qrow = wave >= 2 && wave < 4;
+  const int rblk = wave & 1;  // row waves: token rows 32 rblk .. +31
+  const int ob = wave - 4;    // owners: state tiles 2 ob, 2 ob + 1
+  const bool owns = !rowwave && 2 * ob < NRT;
+  const int vcol = 2 * Hk * D + h * D + kCols * cb;
+  const int acol = ((qrow ? 0 : Hk) + g) * D;
 
-  __shared__ __align__(16) bf16 s_hT[2][kCols][D + 8];   // state block, transposed [j][i], hi/lo
-  __shared__ __align__(16) bf16 s_XT[2][kCols][kLP];     // X block, transposed [j][s], hi/lo
+  __shared__ __align__(16) bf16 s_hT[2][kCols][D + 8];  // state block h^T, hi/lo
+  __shared__ __align__(16) bf16 s_XT[2][kCols][kLP];    // X^T, hi/lo
 
-  float *hs = p.h_state[seq] + (size_t)h * D * D + kCols * cb;
-  floatx4 hacc[2];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    hacc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (wave < F::NRT) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) hacc[ct][rr] = hs[(size_t)(16 * wave + 4 * lg + rr) * D + 16 * ct + lr];
-      const float v[4] = {hacc[ct][0], hacc[ct][1], hacc[ct][2], hacc[ct][3]};
-      store_split4(&s_hT[0][16 * ct + lr][16 * wave + 4 * lg], &s_hT[1][16 * ct + lr][16 * wave + 4 * lg], v);
-    }
-  }
-  __syncthreads();
-
-  TO *o = static_cast<TO *>(p.o);
-  // Two operand buffers in ping-pong: the loads for chunk c+1 are in flight while
-  // chunk c computes, and no register copy forces them to land early.
-  F bufA, bufB;
-  auto chunk_load = [&](F &f, int c) {
-    const int cc = min(c, nch - 1);  // past the end: re-load the last chunk, unused
-    load_chunk<D, TY>(f, p, units, c_first + cc, seq_t0 + kC * cc, min(kC, seq_len - kC * cc), h, g, cb, wave,
-                      lr, lg);
+  const TY *y = static_cast<const TY *>(p.y);
+  auto unit_of = [&](int c) { return units + ((size_t)(c_first + c) * Hv + h) * unit_bytes(D); };
+  auto gam_of = [&](int c) {
+    return reinterpret_cast<const float *>(reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC + 2 * kC * kC);
   };
-  chunk_load(bufA, 0);
-#pragma unroll 1
-  for (int c = 0; c < nch; c += 2) {
-    chunk_load(bufB, c + 1);
-    spine_step<D, TY, TO>(bufA, hacc, s_hT, s_XT, o, p.scale, Hv, h, cb, wave, lr, lg);
-    if (c + 1 >= nch) break;
-    chunk_load(bufA, c + 2);
-    spine_step<D, TY, TO>(bufB, hacc, s_hT, s_XT, o, p.scale, Hv, h, cb, wave, lr, lg);
-  }
-  if (wave < F::NRT) {
+  auto chunk_t0 = [&](int c) { return seq_t0 + kC * c; };
+  auto chunk_len = [&](int c) { return min(kC, seq_len - kC * c); };
+
+  Slot sl;
+  SlotX sx;
+  float gcv[2] = {0.0f, 0.0f};  // owners: Gam_63 of the chunks of parity 0 / 1
+  // K or Q rows of a chunk; rows past its end are clamped into it (they only meet
+  // zero columns of E and MT, and are not stored)
+  auto fetch_rows = [&](int c) {
+    const int t0 = chunk_t0(c), L = chunk_len(c);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const TY *ar = y + (size_t)(t0 + min(32 * rblk + 16 * rt + lr, L - 1)) * CD + acol + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) load_row(sl, rt * KS + ks, ar + 32 * ks);
+    }
+  };
+  // K-row waves: V[t][j] for t = 32 rblk + 16 rt + 4 lg + r, j = 16 ct + lr, and Gam
+  auto fetch_v = [&](int c) {
+    const int t0 = chunk_t0(c), L = chunk_len(c);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const TY *vr = y + (size_t)(t0 + min(32 * rblk + 16 * rt + 4 * lg + r, L - 1)) * CD + vcol + lr;
+        lane32(sx[2 * rt], r) = load_raw(vr);
+        lane32(sx[2 * rt + 1], r) = load_raw(vr + 16);
+      }
+    const float *Gam = gam_of(c);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) sx[4 + rt] = *reinterpret_cast<const uint4 *>(Gam + 32 * rblk + 16 * rt + 4 * lg);
+  };
+  // Q-row waves: Gam of their token rows, and MT fragments of their two tiles
+  auto fetch_gt = [&](int c) {
+    const float *Gam = gam_of(c);
+    sx[8].x = __builtin_bit_cast(uint32_t, Gam[32 * rblk + lr]);
+    sx[8].y = __builtin_bit_cast(uint32_t, Gam[32 * rblk + 16 + lr]);
+  };
+  auto fetch_mt = [&](int c) {
+    const bf16 *MT = reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        sx[4 * rt + ks] = *reinterpret_cast<const uint4 *>(MT + frag_off(2 * rblk + rt, ks, 2, lane));
+        sx[4 * rt + 2 + ks] = *reinterpret_cast<const uint4 *>(MT + kC * kC + frag_off(2 * rblk + rt, ks, 2, lane));
+      }
+  };
+  // owners: E fragments of their two tiles into half `par` of the slot, and Gam_63
+  auto fetch_e = [&](int par, int c) {
+    const bf16 *E = reinterpret_cast<const bf16 *>(unit_of(c));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        sl[8 * par + 4 * t + qq] = *reinterpret_cast<const uint4 *>(E + frag_off(2 * ob + t, qq, 2, lane));
+        sl[8 * par + 4 * t + 2 + qq] =
+            *reinterpret_cast<const uint4 *>(E + D * kC + frag_off(2 * ob + t, qq, 2, lane));
+      }
+    gcv[par] = gam_of(c)[kC - 1];
+  };
+
+  // Each role runs its own loop (the waves of a role never take another role's
+  // branch), with the same two barriers per chunk in every loop; separate loops
+  // let the compiler track each role's loads, waits and registers on their own.
+  gptr<float> hs = to_global(p.h_state[seq]) + (size_t)h * D * D + kCols * cb;
+  TO *o = static_cast<TO *>(p.o);
+  const size_t ostride = (size_t)Hv * D;
+
+  // stage-1 products of a row wave: acc[rt][ct][0] takes the h_hi terms
+  auto row_products = [&](floatx4 (&acc)[2][2][2], bool qw) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) acc[rt][ct][0] = acc[rt][ct][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 bh[2], bl[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        bh[ct] = *reinterpret_cast<const bf16x8 *>(&s_hT[0][16 * ct + lr][32 * ks + 8 * lg]);
+        bl[ct] = *reinterpret_cast<const bf16x8 *>(&s_hT[1][16 * ct + lr][32 * ks + 8 * lg]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        bf16x8 ah, al;
+        row_split<TY>(sl, rt * KS + ks, ah, al);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          if (qw) {  // R^T = h^T Q^T
+            acc[rt][ct][0] = mfma16(bh[ct], ah, acc[rt][ct][0]);
+            acc[rt][ct][1] = mfma16(bl[ct], ah, acc[rt][ct][1]);
+            if (SP) acc[rt][ct][1] = mfma16(bh[ct], al, acc[rt][ct][1]);
+          } else {   // P = K h
+            acc[rt][ct][0] = mfma16(ah, bh[ct], acc[rt][ct][0]);
+            acc[rt][ct][1] = mfma16(ah, bl[ct], acc[rt][ct][1]);
+            if (SP) acc[rt][ct][1] = mfma16(al, bh[ct], acc[rt][ct][1]);
+          }
+        }
+      }
+    }
+  };
+  auto load_xt = [&](bf16x8 (&xh)[2][2], bf16x8 (&xl)[2][2]) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) hs[(size_t)(16 * wave + 4 * lg + rr) * D + 16 * ct + lr] = hacc[ct][rr];
+      for (int ks = 0; ks < 2; ++ks) {
+        xh[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[0][16 * ct + lr][32 * ks + 8 * lg]);
+        xl[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[1][16 * ct + lr][32 * ks + 8 * lg]);
+      }
+  };
+
+  if (rowwave && !qrow) {
+    // ---------------- K-row waves ----------------
+    fetch_rows(0);
+    fetch_v(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+      floatx4 acc[2][2][2];
+      row_products(acc, false);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int tb0 = 32 * rblk + 16 * rt;
+        const float4 gq = __builtin_bit_cast(float4, sx[4 + rt]);
+        const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          float X[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            X[r] = widen<TY>(lane32(sx[2 * rt + ct], r)) - gv[r] * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
+          store_split4(&s_XT[0][16 * ct + lr][tb0 + 4 * lg], &s_XT[1][16 * ct + lr][tb0 + 4 * lg], X);
+        }
+      }
+      __syncthreads();
+      // no stage-2 work: fetch the next chunk (past the end: the last one again, unused)
+      const int cn = min(c + 1, nch - 1);
+      fetch_rows(cn);
+      fetch_v(cn);
+      __syncthreads();
+    }
+  } else if (qrow) {
+    // ---------------- Q-row waves ----------------
+    fetch_rows(0);
+    fetch_gt(0);
+    fetch_mt(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+      const int L = chunk_len(c), cn = min(c + 1, nch - 1);
+      floatx4 acc[2][2][2], Ot[2][2];
+      row_products(acc, true);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float gt = __builtin_bit_cast(float, rt == 0 ? sx[8].x : sx[8].y);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ot[rt][ct][r] = gt * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
+      }
+      __syncthreads();
+      bf16x8 xh[2][2], xl[2][2];
+      load_xt(xh, xl);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 mh = as_bf16x8(sx[4 * rt + ks]), ml = as_bf16x8(sx[4 * rt + 2 + ks]);
+            Ot[rt][ct] = mfma16(xh[ct][ks], mh, Ot[rt][ct]);
+            Ot[rt][ct] = mfma16(xl[ct][ks], mh, Ot[rt][ct]);
+            Ot[rt][ct] = mfma16(xh[ct][ks], ml, Ot[rt][ct]);
+          }
+      // the next chunk's operands, issued while the O products are in flight (a
+      // full vector-memory queue then stalls nothing that waits for them)
+      fetch_rows(cn);
+      fetch_gt(cn);
+      fetch_mt(cn);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int t = 32 * rblk + 16 * rt + lr;
+        TO *orow = o + (size_t)(chunk_t0(c) + t) * ostride + (size_t)h * D + kCols * cb;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float v[4] = {p.scale * Ot[rt][ct][0], p.scale * Ot[rt][ct][1], p.scale * Ot[rt][ct][2],
+                              p.scale * Ot[rt][ct][3]};
+          if (t < L) store4(orow + 16 * ct + 4 * lg, v);
+        }
+      }
+      __syncthreads();
+    }
+  } else if (owns) {
+    // ---------------- owners ----------------
+    floatx4 hacc[2][2];
+    fetch_e(0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hacc[t][ct][r] = hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 16 * ct + lr];
+        const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
+        store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
+                     &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
+      }
+    __syncthreads();
+    // PAR = c & 1 as a compile-time constant: the two E halves are fixed registers
+    auto owner_chunk = [&](int c, auto par) {
+      constexpr int PAR = decltype(par)::value;
+      fetch_e(PAR ^ 1, min(c + 1, nch - 1));  // next chunk's E, during stage 1
+      __syncthreads();
+      bf16x8 xh[2][2], xl[2][2];
+      load_xt(xh, xl);
+      const float gC = gcv[PAR];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          hacc[t][ct] *= gC;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 eh = as_bf16x8(sl[8 * PAR + 4 * t + ks]), el = as_bf16x8(sl[8 * PAR + 4 * t + 2 + ks]);
+            hacc[t][ct] = mfma16(eh, xh[ct][ks], hacc[t][ct]);
+            hacc[t][ct] = mfma16(eh, xl[ct][ks], hacc[t][ct]);
+            hacc[t][ct] = mfma16(el, xh[ct][ks], hacc[t][ct]);
+          }
+          const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
+          store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
+                       &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
+        }
+      __syncthreads();
+    };
+#pragma unroll 1
+    for (int c = 0; c < nch; c += 2) {
+      owner_chunk(c, std::integral_constant<int, 0>());
+      if (c + 1 >= nch) break;
+      owner_chunk(c + 1, std::integral_constant<int, 1>());
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 16 * ct + lr] = hacc[t][ct][r];
+  } else {
+    // waves without state rows (d_k < 128): keep the barrier count
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+      __syncthreads();
+      __syncthreads();
+    }
   }
 }
 
