@@ -431,84 +431,85 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
 // ---- 3. the serial pass over chunks -------------------------------------------
 // 512 threads per (sequence, value head, 32-column block of d_v).  Columns of h
 // evolve independently, so a d_v-wide state splits over d_v / 32 workgroups.
-//   waves 0-3 ("row waves"): token rows 32 (w & 1) .. +31 of K (w < 2) or Q (w >= 2),
-//       both 16-column tiles.  Stage 1: P = K h -> X = V - Gam P -> LDS (K), or
-//       R^T = h^T Q^T (Q).  Stage 2 (Q): O^T = Gam R^T + X^T MT^T, stored.
-//   waves 4-7 ("owners"): state rows 32 (w - 4) .. +31 of the block live in their
-//       MFMA accumulators.  Stage 2: h <- Gam_63 h + E X, copied as bf16 hi/lo h^T
-//       to LDS for the next stage 1.
-// One barrier after each stage.  Each wave loads exactly the operands it consumes
-// (84 KiB per chunk and workgroup at d = 128, nothing read twice).  The per-CU
-// vector-memory path moves about 64 B per clock, so these loads take as long as
-// the arithmetic; they are issued by waves that have nothing else to do at that
-// moment, so that a full queue stalls nobody on the critical path: owners fetch
-// the next chunk's E during stage 1 (double-buffered; chunk parity picks the half
-// at compile time, so no register copy forces a load to land early), K-row waves
-// fetch the next K rows, V and Gam during stage 2, Q-row waves the next Q rows and
-// MT once their O products are in flight.  O is formed transposed,
-// so a lane holds four consecutive columns of one token row and stores them at once.
+//   waves 0-1 ("K-row waves"): token rows 32 w .. +31.  Stage 1: P^T = h^T K^T,
+//       X = V - Gam P -> LDS.  Stage 2: fetch the next chunk's K rows, V, Gam.
+//   waves 2-3 ("Q-row waves"): token rows 32 (w - 2) .. +31.  Stage 1: R^T = h^T Q^T,
+//       then fetch the next chunk's Q rows and Gam.  Stage 2: O^T = Gam R^T +
+//       X^T MT^T, stored; then fetch the next chunk's MT.
+//   waves 4-7 ("owners"): state rows 32 (w - 4) .. +31 of the block live in MFMA
+//       accumulators.  Stage 1: fetch the next chunk's E (double-buffered).
+//       Stage 2: h <- Gam_63 h + E X, copied as bf16 hi/lo h^T to LDS.
+// One barrier after each stage; each role runs its own loop, with the same two
+// barriers per chunk, so the compiler tracks each role's loads, waits and
+// registers on their own.  Each wave loads exactly the operands it consumes (84 KiB
+// per chunk and workgroup at d = 128, nothing read twice), all as 16-byte
+// accesses: the per-CU vector-memory path spends about as long on a 2-byte load
+// instruction as on a 16-byte one, and its throughput sets the pace of a chunk.
+// Loads for chunk c+1 go out right after the last use of the registers they fill
+// and land while chunk c computes.
+//
+// Column order: inside the workgroup, state column j (0..31) of the block sits at
+// position jj = 16 (j & 1) + j / 2, so MFMA column tile ct holds the columns of
+// parity ct.  The products with h are taken transposed (h^T times rows), and a
+// lane then holds, for one token row, positions 16 ct + 4 lg + r (r = 0..3,
+// ct = 0..1), which are the 8 consecutive columns 8 lg .. 8 lg + 7: one 16-byte V
+// load and one 16-byte O store per token tile.
 constexpr int kCols = 32;  // state columns per workgroup
 
-// Raw 16-byte register slots.  Row waves keep their K or Q rows in `sl` (bf16:
-// entry rt * KS + ks; fp32: the pair 2 (rt * KS + ks) + {0, 1}); owners keep E
-// fragments there ([parity][tile][hi k0, hi k1, lo k0, lo k1], entry 8 parity +
-// 4 tile + i).  `sx` holds V (16 values, one per 32-bit lane of entries 0-3) and
-// Gam (entries 4-5) for K-row waves, MT fragments (entries 4 rt + i) and Gam
-// (entry 8) for Q-row waves.
-typedef uint4 Slot[16];
-typedef uint4 SlotX[9];
-
-__device__ __forceinline__ void load_row(Slot &sl, int i, const bf16 *p) {
-  sl[i] = *reinterpret_cast<const uint4 *>(p);
-}
-__device__ __forceinline__ void load_row(Slot &sl, int i, const float *p) {
-  sl[2 * i] = reinterpret_cast<const uint4 *>(p)[0];
-  sl[2 * i + 1] = reinterpret_cast<const uint4 *>(p)[1];
+// K or Q row fragments (bf16: one 16-byte word, fp32: two) and V words, kept raw
+// until used.
+template <typename TY>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  uint4 w;
+};
+template <>
+struct Raw8<float> {
+  uint4 w0, w1;
+};
+__device__ __forceinline__ void load8(Raw8<bf16> &r, const bf16 *p) { r.w = *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void load8(Raw8<float> &r, const float *p) {
+  r.w0 = reinterpret_cast<const uint4 *>(p)[0];
+  r.w1 = reinterpret_cast<const uint4 *>(p)[1];
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
-template <typename TY>
-__device__ __forceinline__ void row_split(const Slot &sl, int i, bf16x8 &hi, bf16x8 &lo) {
-  if constexpr (std::is_same<TY, bf16>::value) {
-    hi = as_bf16x8(sl[i]);
-    lo = hi;  // unused: bf16 activations are exact
-  } else {
-    const float4 a = __builtin_bit_cast(float4, sl[2 * i]), b = __builtin_bit_cast(float4, sl[2 * i + 1]);
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// the 8 values as floats
+__device__ __forceinline__ void unpack8(const Raw8<bf16> &r, float v[8]) {
+  const bf16x8 b = as_bf16x8(r.w);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bf16 h, l;
-      split_bf16(v[e], h, l);
-      hi[e] = h;
-      lo[e] = l;
-    }
+  for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
+}
+__device__ __forceinline__ void unpack8(const Raw8<float> &r, float v[8]) {
+  const float4 a = __builtin_bit_cast(float4, r.w0), b = __builtin_bit_cast(float4, r.w1);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+// as an MFMA operand: bf16 is exact (lo unused), fp32 splits into hi + lo
+__device__ __forceinline__ void split8(const Raw8<bf16> &r, bf16x8 &hi, bf16x8 &lo) {
+  hi = as_bf16x8(r.w);
+  lo = hi;
+}
+__device__ __forceinline__ void split8(const Raw8<float> &r, bf16x8 &hi, bf16x8 &lo) {
+  float v[8];
+  unpack8(r, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16 h, l;
+    split_bf16(v[e], h, l);
+    hi[e] = h;
+    lo[e] = l;
   }
 }
-// One activation, loaded raw into a 32-bit register and widened at use.
-__device__ __forceinline__ uint32_t load_raw(const bf16 *p) { return *reinterpret_cast<const uint16_t *>(p); }
-__device__ __forceinline__ uint32_t load_raw(const float *p) { return *reinterpret_cast<const uint32_t *>(p); }
-template <typename TY>
-__device__ __forceinline__ float widen(uint32_t u) {
-  if constexpr (std::is_same<TY, bf16>::value) return __builtin_bit_cast(float, u << 16);
-  else return __builtin_bit_cast(float, u);
-}
-__device__ __forceinline__ uint32_t &lane32(uint4 &u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-__device__ __forceinline__ uint32_t lane32(const uint4 &u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
 
-__device__ __forceinline__ void store4(float *p, const float v[4]) {
-  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ void store8(float *p, const float v[8]) {
+  reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
-__device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
-  union {
-    bf16 b[4];
-    uint2 u;
-  } w;
+__device__ __forceinline__ void store8(bf16 *p, const float v[8]) {
+  bf16x8 b;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) w.b[e] = (bf16)v[e];
-  *reinterpret_cast<uint2 *>(p) = w.u;
+  for (int e = 0; e < 8; ++e) b[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x8 *>(p) = b;
 }
 
 template <int D, typename TY, typename TO>
@@ -537,92 +538,46 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   const int g = h / G;
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const bool rowwave = wave < 4, qrow = wave >= 2 && wave < 4;
   const int rblk = wave & 1;  // row waves: token rows 32 rblk .. +31
   const int ob = wave - 4;    // owners: state tiles 2 ob, 2 ob + 1
-  const bool owns = !rowwave && 2 * ob < NRT;
   const int vcol = 2 * Hk * D + h * D + kCols * cb;
-  const int acol = ((qrow ? 0 : Hk) + g) * D;
 
-  __shared__ __align__(16) bf16 s_hT[2][kCols][D + 8];  // state block h^T, hi/lo
-  __shared__ __align__(16) bf16 s_XT[2][kCols][kLP];    // X^T, hi/lo
+  __shared__ __align__(16) bf16 s_hT[2][kCols][D + 8];  // state block h^T [jj][i], hi/lo
+  __shared__ __align__(16) bf16 s_XT[2][kCols][kLP];    // X^T [jj][t], hi/lo
 
   const TY *y = static_cast<const TY *>(p.y);
+  TO *o = static_cast<TO *>(p.o);
+  const size_t ostride = (size_t)Hv * D;
+  gptr<float> hs = to_global(p.h_state[seq]) + (size_t)h * D * D + kCols * cb;
   auto unit_of = [&](int c) { return units + ((size_t)(c_first + c) * Hv + h) * unit_bytes(D); };
   auto gam_of = [&](int c) {
     return reinterpret_cast<const float *>(reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC + 2 * kC * kC);
   };
   auto chunk_t0 = [&](int c) { return seq_t0 + kC * c; };
   auto chunk_len = [&](int c) { return min(kC, seq_len - kC * c); };
+  // row waves: token row of tile rt in chunk c, clamped into the chunk (rows past
+  // its end only meet zero columns of E and MT, and are not stored)
+  auto row_of = [&](int c, int rt) { return chunk_t0(c) + min(32 * rblk + 16 * rt + lr, chunk_len(c) - 1); };
 
-  Slot sl;
-  SlotX sx;
-  float gcv[2] = {0.0f, 0.0f};  // owners: Gam_63 of the chunks of parity 0 / 1
-  // K or Q rows of a chunk; rows past its end are clamped into it (they only meet
-  // zero columns of E and MT, and are not stored)
-  auto fetch_rows = [&](int c) {
-    const int t0 = chunk_t0(c), L = chunk_len(c);
+  // ---- row waves: shared pieces ----
+  Raw8<TY> rows[2][KS];
+  float gt[2];
+  auto fetch_rows = [&](int c, int col) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-      const TY *ar = y + (size_t)(t0 + min(32 * rblk + 16 * rt + lr, L - 1)) * CD + acol + 8 * lg;
+      const TY *ar = y + (size_t)row_of(c, rt) * CD + col + 8 * lg;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) load_row(sl, rt * KS + ks, ar + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks) load8(rows[rt][ks], ar + 32 * ks);
     }
   };
-  // K-row waves: V[t][j] for t = 32 rblk + 16 rt + 4 lg + r, j = 16 ct + lr, and Gam
-  auto fetch_v = [&](int c) {
-    const int t0 = chunk_t0(c), L = chunk_len(c);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const TY *vr = y + (size_t)(t0 + min(32 * rblk + 16 * rt + 4 * lg + r, L - 1)) * CD + vcol + lr;
-        lane32(sx[2 * rt], r) = load_raw(vr);
-        lane32(sx[2 * rt + 1], r) = load_raw(vr + 16);
-      }
-    const float *Gam = gam_of(c);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) sx[4 + rt] = *reinterpret_cast<const uint4 *>(Gam + 32 * rblk + 16 * rt + 4 * lg);
-  };
-  // Q-row waves: Gam of their token rows, and MT fragments of their two tiles
   auto fetch_gt = [&](int c) {
     const float *Gam = gam_of(c);
-    sx[8].x = __builtin_bit_cast(uint32_t, Gam[32 * rblk + lr]);
-    sx[8].y = __builtin_bit_cast(uint32_t, Gam[32 * rblk + 16 + lr]);
+    gt[0] = Gam[32 * rblk + lr];
+    gt[1] = Gam[32 * rblk + 16 + lr];
   };
-  auto fetch_mt = [&](int c) {
-    const bf16 *MT = reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        sx[4 * rt + ks] = *reinterpret_cast<const uint4 *>(MT + frag_off(2 * rblk + rt, ks, 2, lane));
-        sx[4 * rt + 2 + ks] = *reinterpret_cast<const uint4 *>(MT + kC * kC + frag_off(2 * rblk + rt, ks, 2, lane));
-      }
-  };
-  // owners: E fragments of their two tiles into half `par` of the slot, and Gam_63
-  auto fetch_e = [&](int par, int c) {
-    const bf16 *E = reinterpret_cast<const bf16 *>(unit_of(c));
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        sl[8 * par + 4 * t + qq] = *reinterpret_cast<const uint4 *>(E + frag_off(2 * ob + t, qq, 2, lane));
-        sl[8 * par + 4 * t + 2 + qq] =
-            *reinterpret_cast<const uint4 *>(E + D * kC + frag_off(2 * ob + t, qq, 2, lane));
-      }
-    gcv[par] = gam_of(c)[kC - 1];
-  };
-
-  // Each role runs its own loop (the waves of a role never take another role's
-  // branch), with the same two barriers per chunk in every loop; separate loops
-  // let the compiler track each role's loads, waits and registers on their own.
-  gptr<float> hs = to_global(p.h_state[seq]) + (size_t)h * D * D + kCols * cb;
-  TO *o = static_cast<TO *>(p.o);
-  const size_t ostride = (size_t)Hv * D;
-
-  // stage-1 products of a row wave: acc[rt][ct][0] takes the h_hi terms
-  auto row_products = [&](floatx4 (&acc)[2][2][2], bool qw) {
+  // P^T or R^T = h^T (rows)^T: acc[rt][ct][0] takes the h_hi terms, [1] the rest;
+  // lane holds position 16 ct + 4 lg + r of token 32 rblk + 16 rt + lr
+  auto row_products = [&](floatx4 (&acc)[2][2][2]) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -638,18 +593,12 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         bf16x8 ah, al;
-        row_split<TY>(sl, rt * KS + ks, ah, al);
+        split8(rows[rt][ks], ah, al);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          if (qw) {  // R^T = h^T Q^T
-            acc[rt][ct][0] = mfma16(bh[ct], ah, acc[rt][ct][0]);
-            acc[rt][ct][1] = mfma16(bl[ct], ah, acc[rt][ct][1]);
-            if (SP) acc[rt][ct][1] = mfma16(bh[ct], al, acc[rt][ct][1]);
-          } else {   // P = K h
-            acc[rt][ct][0] = mfma16(ah, bh[ct], acc[rt][ct][0]);
-            acc[rt][ct][1] = mfma16(ah, bl[ct], acc[rt][ct][1]);
-            if (SP) acc[rt][ct][1] = mfma16(al, bh[ct], acc[rt][ct][1]);
-          }
+          acc[rt][ct][0] = mfma16(bh[ct], ah, acc[rt][ct][0]);
+          acc[rt][ct][1] = mfma16(bl[ct], ah, acc[rt][ct][1]);
+          if (SP) acc[rt][ct][1] = mfma16(bh[ct], al, acc[rt][ct][1]);
         }
       }
     }
@@ -664,39 +613,61 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       }
   };
 
-  if (rowwave && !qrow) {
+  if (wave < 2) {
     // ---------------- K-row waves ----------------
-    fetch_rows(0);
+    const int kcol = (Hk + g) * D;
+    Raw8<TY> vv[2];
+    auto fetch_v = [&](int c) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) load8(vv[rt], y + (size_t)row_of(c, rt) * CD + vcol + 8 * lg);
+    };
+    fetch_rows(0, kcol);
     fetch_v(0);
+    fetch_gt(0);
     __syncthreads();
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
       floatx4 acc[2][2][2];
-      row_products(acc, false);
+      row_products(acc);
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const int tb0 = 32 * rblk + 16 * rt;
-        const float4 gq = __builtin_bit_cast(float4, sx[4 + rt]);
-        const float gv[4] = {gq.x, gq.y, gq.z, gq.w};
+        const int t = 32 * rblk + 16 * rt + lr;
+        float v[8];
+        unpack8(vv[rt], v);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          float X[4];
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            X[r] = widen<TY>(lane32(sx[2 * rt + ct], r)) - gv[r] * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
-          store_split4(&s_XT[0][16 * ct + lr][tb0 + 4 * lg], &s_XT[1][16 * ct + lr][tb0 + 4 * lg], X);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const float X = v[2 * r + ct] - gt[rt] * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
+            bf16 hi, lo;
+            split_bf16(X, hi, lo);
+            s_XT[0][16 * ct + 4 * lg + r][t] = hi;
+            s_XT[1][16 * ct + 4 * lg + r][t] = lo;
+          }
       }
       __syncthreads();
       // no stage-2 work: fetch the next chunk (past the end: the last one again, unused)
       const int cn = min(c + 1, nch - 1);
-      fetch_rows(cn);
+      fetch_rows(cn, kcol);
       fetch_v(cn);
+      fetch_gt(cn);
       __syncthreads();
     }
-  } else if (qrow) {
+  } else if (wave < 4) {
     // ---------------- Q-row waves ----------------
-    fetch_rows(0);
+    const int qcol = g * D;
+    uint4 mt[2][4];  // MT fragments of the two token tiles: hi k0, hi k1, lo k0, lo k1
+    auto fetch_mt = [&](int c) {
+      const bf16 *MT = reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          mt[rt][ks] = *reinterpret_cast<const uint4 *>(MT + frag_off(2 * rblk + rt, ks, 2, lane));
+          mt[rt][2 + ks] = *reinterpret_cast<const uint4 *>(MT + kC * kC + frag_off(2 * rblk + rt, ks, 2, lane));
+        }
+    };
+    fetch_rows(0, qcol);
     fetch_gt(0);
     fetch_mt(0);
     __syncthreads();
@@ -704,15 +675,16 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     for (int c = 0; c < nch; ++c) {
       const int L = chunk_len(c), cn = min(c + 1, nch - 1);
       floatx4 acc[2][2][2], Ot[2][2];
-      row_products(acc, true);
+      row_products(acc);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const float gt = __builtin_bit_cast(float, rt == 0 ? sx[8].x : sx[8].y);
+      for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Ot[rt][ct][r] = gt * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
-      }
+          for (int r = 0; r < 4; ++r) Ot[rt][ct][r] = gt[rt] * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
+      // this chunk's Q rows and Gam are consumed
+      fetch_rows(cn, qcol);
+      fetch_gt(cn);
       __syncthreads();
       bf16x8 xh[2][2], xl[2][2];
       load_xt(xh, xl);
@@ -722,31 +694,40 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 mh = as_bf16x8(sx[4 * rt + ks]), ml = as_bf16x8(sx[4 * rt + 2 + ks]);
+            const bf16x8 mh = as_bf16x8(mt[rt][ks]), ml = as_bf16x8(mt[rt][2 + ks]);
             Ot[rt][ct] = mfma16(xh[ct][ks], mh, Ot[rt][ct]);
             Ot[rt][ct] = mfma16(xl[ct][ks], mh, Ot[rt][ct]);
             Ot[rt][ct] = mfma16(xh[ct][ks], ml, Ot[rt][ct]);
           }
-      // the next chunk's operands, issued while the O products are in flight (a
-      // full vector-memory queue then stalls nothing that waits for them)
-      fetch_rows(cn);
-      fetch_gt(cn);
-      fetch_mt(cn);
+      fetch_mt(cn);  // issued while the O products are in flight
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int t = 32 * rblk + 16 * rt + lr;
-        TO *orow = o + (size_t)(chunk_t0(c) + t) * ostride + (size_t)h * D + kCols * cb;
+        float v[8];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const float v[4] = {p.scale * Ot[rt][ct][0], p.scale * Ot[rt][ct][1], p.scale * Ot[rt][ct][2],
-                              p.scale * Ot[rt][ct][3]};
-          if (t < L) store4(orow + 16 * ct + 4 * lg, v);
-        }
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[2 * r + ct] = p.scale * Ot[rt][ct][r];
+        if (t < L) store8(o + (size_t)(chunk_t0(c) + t) * ostride + (size_t)h * D + kCols * cb + 8 * lg, v);
       }
       __syncthreads();
     }
-  } else if (owns) {
+  } else if (2 * ob < NRT) {
     // ---------------- owners ----------------
+    uint4 ef[2][2][4];  // E fragments [parity][tile][hi k0, hi k1, lo k0, lo k1]
+    float gcv[2];       // Gam_63 of the chunks of parity 0 / 1
+    auto fetch_e = [&](int par, int c) {
+      const bf16 *E = reinterpret_cast<const bf16 *>(unit_of(c));
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          ef[par][t][qq] = *reinterpret_cast<const uint4 *>(E + frag_off(2 * ob + t, qq, 2, lane));
+          ef[par][t][2 + qq] = *reinterpret_cast<const uint4 *>(E + D * kC + frag_off(2 * ob + t, qq, 2, lane));
+        }
+      gcv[par] = gam_of(c)[kC - 1];
+    };
+    // lane holds h[16 tile + 4 lg + r][column 2 lr + ct] (position 16 ct + lr)
     floatx4 hacc[2][2];
     fetch_e(0, 0);
 #pragma unroll
@@ -754,13 +735,13 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hacc[t][ct][r] = hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 16 * ct + lr];
+        for (int r = 0; r < 4; ++r) hacc[t][ct][r] = hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct];
         const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
         store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
                      &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
       }
     __syncthreads();
-    // PAR = c & 1 as a compile-time constant: the two E halves are fixed registers
+    // PAR = c & 1 as a compile-time constant: the two E buffers are fixed registers
     auto owner_chunk = [&](int c, auto par) {
       constexpr int PAR = decltype(par)::value;
       fetch_e(PAR ^ 1, min(c + 1, nch - 1));  // next chunk's E, during stage 1
@@ -775,7 +756,7 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
           hacc[t][ct] *= gC;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 eh = as_bf16x8(sl[8 * PAR + 4 * t + ks]), el = as_bf16x8(sl[8 * PAR + 4 * t + 2 + ks]);
+            const bf16x8 eh = as_bf16x8(ef[PAR][t][ks]), el = as_bf16x8(ef[PAR][t][2 + ks]);
             hacc[t][ct] = mfma16(eh, xh[ct][ks], hacc[t][ct]);
             hacc[t][ct] = mfma16(eh, xl[ct][ks], hacc[t][ct]);
             hacc[t][ct] = mfma16(el, xh[ct][ks], hacc[t][ct]);
@@ -797,7 +778,7 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 16 * ct + lr] = hacc[t][ct][r];
+        for (int r = 0; r < 4; ++r) hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct] = hacc[t][ct][r];
   } else {
     // waves without state rows (d_k < 128): keep the barrier count
     __syncthreads();
