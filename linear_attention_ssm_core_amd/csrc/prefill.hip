@@ -266,12 +266,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     frag8(Kb + (size_t)min(sr, L - 1) * CD + i0, kth[m], ktl[m]);
   }
   // wave w owns row block w of Q K^T -> M and of K K^T -> Abar
+  // (the wave's own K rows are loaded on their own: picking them out of kh by the
+  // wave index would be a run-time index into a register array, i.e. scratch memory)
   const int ti = wave;
-  bf16x8 qh[KS], ql[KS], kh[4][KS], kl[4][KS];
+  bf16x8 qh[KS], ql[KS], kih[KS], kil[KS], kh[4][KS], kl[4][KS];
   {
     const TY *qrow = Qb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
+    const TY *kirow = Kb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) frag8(qrow + 32 * ks, qh[ks], ql[ks]);
+    for (int ks = 0; ks < KS; ++ks) {
+      frag8(qrow + 32 * ks, qh[ks], ql[ks]);
+      frag8(kirow + 32 * ks, kih[ks], kil[ks]);
+    }
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
       const TY *krow = Kb + (size_t)min(16 * tj + lr, L - 1) * CD + 8 * lg;
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         aq = mma<SP, SP>(aq, qh[ks], ql[ks], kh[tj][ks], kl[tj][ks]);
-        ak = mma<SP, SP>(ak, kh[ti][ks], kl[ti][ks], kh[tj][ks], kl[tj][ks]);
+        ak = mma<SP, SP>(ak, kih[ks], kil[ks], kh[tj][ks], kl[tj][ks]);
       }
     }
 #pragma unroll
