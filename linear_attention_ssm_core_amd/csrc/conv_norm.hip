@@ -16,8 +16,10 @@
 namespace gdn {
 namespace {
 
-constexpr int kConvRows = 32;   // packed rows per workgroup
-constexpr int kConvGroup = 8;   // rows whose loads are issued together
+// Packed rows per workgroup: every row load of a thread is issued at once (kept
+// raw until used), so a 256-thread workgroup has 128 KiB (bf16 input) in flight.
+template <typename TA>
+constexpr int conv_rows() { return sizeof(TA) == 2 ? 32 : 16; }
 
 // Eight consecutive channels of one row, widened to fp32.
 __device__ __forceinline__ void load8(const bf16 *p, float v[8]) {
@@ -39,14 +41,40 @@ __device__ __forceinline__ void store8(float *p, const float v[8]) {
   reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
   reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
+// raw 8-channel words, widened when used
+template <typename TA>
+struct Raw8;
+template <>
+struct Raw8<bf16> {
+  uint4 w;
+  __device__ __forceinline__ void load(const bf16 *p) { w = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void get(float v[8]) const {
+    const bf16x8 r = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)r[e];
+  }
+};
+template <>
+struct Raw8<float> {
+  uint4 w0, w1;
+  __device__ __forceinline__ void load(const float *p) {
+    w0 = reinterpret_cast<const uint4 *>(p)[0];
+    w1 = reinterpret_cast<const uint4 *>(p)[1];
+  }
+  __device__ __forceinline__ void get(float v[8]) const {
+    const float4 a = __builtin_bit_cast(float4, w0), b = __builtin_bit_cast(float4, w1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
 
-// Each thread owns 8 consecutive channels and walks kConvRows packed rows in order
-// with the K-1 previous rows of its channels in registers, so every input row is
-// read once with 16-byte (bf16) loads; a q or k head (d channels) is d/8
-// consecutive lanes, which reduce its squared norm with shuffles.
+// Each thread owns 8 consecutive channels of conv_rows<TA>() consecutive packed
+// rows; every input row is read once with 16-byte loads (plus 3 history rows per
+// workgroup); a q or k head (d channels) is d/8 consecutive lanes, which reduce
+// its squared norm with shuffles.
 template <int D, typename TA, typename TY>
-__global__ __launch_bounds__(256) void conv_l2norm_kernel(ConvLaunch p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void conv_l2norm_kernel(ConvLaunch p) {
   constexpr int TPH = D / 8;  // lanes per head
+  constexpr int R = conv_rows<TA>();
   const int C = p.geo.conv_dim, K = p.geo.K, Hk = p.geo.Hk;
   const int c0 = (blockIdx.y * 256 + threadIdx.x) * 8;
   const bool active = c0 < C;  // uniform per head (C is a multiple of d)
@@ -56,15 +84,9 @@ __global__ __launch_bounds__(256) void conv_l2norm_kernel(ConvLaunch p) {
   const TA *w = static_cast<const TA *>(p.conv_w);
   TY *y = static_cast<TY *>(p.y);
 
-  float wt[4][8];  // tap j of channel cc + e
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wt[j][e] = (j < K) ? ld(w, (size_t)(cc + e) * K + j) : 0.0f;
-
-  const int64_t t0 = (int64_t)blockIdx.x * kConvRows;
-  const int64_t t1 = min((int64_t)p.T, t0 + kConvRows);
-  // sequence of row t0 (invariant cu[lo] <= t0 < cu[hi]), then walk forward
+  const int64_t t0 = (int64_t)blockIdx.x * R;
+  const int64_t t1 = min((int64_t)p.T, t0 + R);
+  // sequence of row t0 (invariant cu[lo] <= t0 < cu[hi])
   int seq;
   {
     int lo = 0, hi = p.n;
@@ -76,65 +98,92 @@ __global__ __launch_bounds__(256) void conv_l2norm_kernel(ConvLaunch p) {
     seq = lo;
   }
   int seq_start = p.cu[seq], seq_end = p.cu[seq + 1];
-  // history window: hist[j] = row t-(K-1)+j of the current sequence
-  float hist[3][8];
-  auto load_hist = [&](int64_t t) {
-    const TA *ring = static_cast<const TA *>(p.conv_state[seq]);
+
+  // taps aligned to rows t-3 .. t: ws[jj] multiplies row t - 3 + jj (zero for the
+  // 4 - K rows before the window), so row offsets are compile-time constants
+  // (loaded unconditionally from a valid tap and zeroed after: a conditional load
+  // would be a branch with a wait for that load on every tap)
+  float ws[4][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = jj - (4 - K);
+      const float v = ld(w, (size_t)(cc + e) * K + max(j, 0));
+      ws[jj][e] = (j >= 0) ? v : 0.0f;
+    }
+
+  // conv + SiLU + L2 norm of row t from rows t-3 .. t (r[3] is row t)
+  auto emit = [&](int64_t t, const float (&r)[4][8]) {
+    float yv[8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc += ws[jj][e] * r[jj][e];
+      yv[e] = silu(acc);
+      ss += yv[e] * yv[e];
+    }
+    if (normalise) {
+#pragma unroll
+      for (int off = 1; off < TPH; off <<= 1) ss += __shfl_xor(ss, off);
+      const float inv = 1.0f / sqrtf(ss + p.l2_eps);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] *= inv;
+    }
+    if (active) store8(y + (size_t)t * C + cc, yv);
+  };
+
+  if (t1 - t0 == R && t0 - 3 >= seq_start && t1 <= seq_end) {
+    // Fast path: the block and its 3 predecessors lie in one sequence.  Every load
+    // is issued first (raw), then the rows are walked with no branch.
+    Raw8<TA> xr[R + 3];  // rows t0 - 3 .. t1 - 1
+#pragma unroll
+    for (int u = 0; u < R + 3; ++u) xr[u].load(x + (size_t)(t0 - 3 + u) * C + cc);
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      float r[4][8];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) xr[u + jj].get(r[jj]);
+      emit(t0 + u, r);
+    }
+    return;
+  }
+
+  // General path (blocks at sequence starts, the ragged tail): row by row, with
+  // rows t-3 .. t-1 of the current sequence in registers (from the conv state
+  // before the sequence's first row; zero where no tap reaches).
+  float r[4][8];
+  auto load_win = [&](int64_t t) {
+    // (through the global address space, so that its loads are not FLAT)
+    const TA *ring = (const TA *)to_global(static_cast<const TA *>(p.conv_state[seq]));
     const int64_t tau = t - seq_start;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      if (j < K - 1) {
-        const int64_t rel = tau - (K - 1) + j;
-        if (rel >= 0) load8(x + (size_t)(seq_start + rel) * C + cc, hist[j]);
-        else load8(ring + (size_t)(K - 1 + rel) * C + cc, hist[j]);
-      }
+    for (int jj = 0; jj < 3; ++jj) {
+      const int64_t rel = tau - 3 + jj;
+      if (rel >= 0) load8(x + (size_t)(seq_start + rel) * C + cc, r[jj]);
+      else if (K - 1 + rel >= 0) load8(ring + (size_t)(K - 1 + rel) * C + cc, r[jj]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[jj][e] = 0.0f;
     }
   };
-  load_hist(t0);
-  for (int64_t tg = t0; tg < t1; tg += kConvGroup) {
-    float xr[kConvGroup][8];
-#pragma unroll
-    for (int u = 0; u < kConvGroup; ++u) {
-      const int64_t t = min(tg + u, t1 - 1);
-      load8(x + (size_t)t * C + cc, xr[u]);
+  load_win(t0);
+#pragma unroll 1
+  for (int64_t t = t0; t < t1; ++t) {
+    while (t >= seq_end) {  // a new sequence starts at t (skip empty ones)
+      ++seq;
+      seq_start = p.cu[seq];
+      seq_end = p.cu[seq + 1];
+      if (t == seq_start && t < seq_end) load_win(t);
     }
+    load8(x + (size_t)t * C + cc, r[3]);
+    emit(t, r);
 #pragma unroll
-    for (int u = 0; u < kConvGroup; ++u) {
-      const int64_t t = tg + u;
-      if (t >= t1) break;
-      while (t >= seq_end) {  // a new sequence starts at t (skip empty ones)
-        ++seq;
-        seq_start = p.cu[seq];
-        seq_end = p.cu[seq + 1];
-        if (t == seq_start && t < seq_end) load_hist(t);
-      }
-      float yv[8];
-      float ss = 0.0f;
+    for (int jj = 0; jj < 3; ++jj)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 3; ++j)
-          if (j < K - 1) acc += wt[j][e] * hist[j][e];
-        acc += (K == 2 ? wt[1][e] : K == 3 ? wt[2][e] : wt[3][e]) * xr[u][e];
-        yv[e] = silu(acc);
-        ss += yv[e] * yv[e];
-      }
-      if (normalise) {
-#pragma unroll
-        for (int off = 1; off < TPH; off <<= 1) ss += __shfl_xor(ss, off);
-        const float inv = 1.0f / sqrtf(ss + p.l2_eps);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) yv[e] *= inv;
-      }
-      if (active) store8(y + (size_t)t * C + cc, yv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (K == 4) { hist[0][e] = hist[1][e]; hist[1][e] = hist[2][e]; hist[2][e] = xr[u][e]; }
-        else if (K == 3) { hist[0][e] = hist[1][e]; hist[1][e] = xr[u][e]; }
-        else { hist[0][e] = xr[u][e]; }
-      }
-    }
+      for (int e = 0; e < 8; ++e) r[jj][e] = r[jj + 1][e];
   }
 }
 
@@ -193,7 +242,8 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormLaunch p) {
 
 template <int D, typename TA>
 hipError_t conv_launch_y(const ConvLaunch &p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.T + kConvRows - 1) / kConvRows), (p.geo.conv_dim / 8 + 255) / 256), block(256);
+  constexpr int R = conv_rows<TA>();
+  const dim3 grid((unsigned)((p.T + R - 1) / R), (p.geo.conv_dim / 8 + 255) / 256), block(256);
   const bool y_bf16 = !p.y_f32 && p.geo.out_bf16;
   if (y_bf16) hipLaunchKernelGGL((conv_l2norm_kernel<D, TA, bf16>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((conv_l2norm_kernel<D, TA, float>), grid, block, 0, stream, p);

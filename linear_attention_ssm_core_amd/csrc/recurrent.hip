@@ -30,6 +30,19 @@ namespace gdn {
 namespace {
 
 constexpr int kSlot = 256;          // threads per value head
+
+__device__ __forceinline__ void store4(float *p, const float v[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
+  union {
+    bf16 b[4];
+    uint2 u;
+  } w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w.b[e] = (bf16)v[e];
+  *reinterpret_cast<uint2 *>(p) = w.u;
+}
 constexpr int kTableSeqs = 128;     // entries per WY pointer table
 
 template <int D, int G, int MAXR, typename TA, typename TO>
@@ -44,6 +57,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   __shared__ float s_qkv[MAXR][NCH];
   __shared__ float s_a[MAXR][G], s_b[MAXR][G];
   __shared__ float s_qk[MAXR];
+  __shared__ float s_zw[MAXR][G * D];  // silu(z) * norm weight of the group's value channels
   __shared__ float4 s_red[2][G][4][CQ][2];
 
   const int Hk = p.geo.Hk, Hv = p.geo.Hv, K = p.geo.K, C = p.geo.conv_dim;
@@ -80,58 +94,92 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   }
   if (nrows == 0) return;  // uniform over the block
 
-  // ---- issue the state loads first; the prologue hides their latency --------
-  const int s = tid / kSlot, t = tid % kSlot;
-  const int h = g * G + s;
-  const int cq = t % CQ, rg = t / CQ;
-  const float *S_in = p.states[i] + (size_t)h * D * D;  // table 0 / decode pointer
-  float4 st_reg[RPT];
-#pragma unroll
-  for (int rr = 0; rr < RPT; ++rr)
-    st_reg[rr] = *reinterpret_cast<const float4 *>(S_in + (size_t)(rr * RG + rg) * D + 4 * cq);
-
-  // ---- prologue: conv + SiLU of the group's channels for every row ----------
+  // ---- prologue loads: conv taps, conv state, input rows, gates, z ------------
+  // All issued first, unconditionally from valid addresses, and kept raw until the
+  // state loads below have been issued: a conditional or converted load would make
+  // the compiler wait for it (and, the counter being in order, for everything
+  // issued before it) in the middle of the prologue.
   const TA *x = static_cast<const TA *>(p.x);
   const TA *w = static_cast<const TA *>(p.conv_w);
   TA *ring = static_cast<TA *>(p.conv_state[i]);
-  for (int cl = tid; cl < NCH; cl += NT) {
-    int c;
-    if (cl < D) c = g * D + cl;
-    else if (cl < 2 * D) c = Hk * D + g * D + (cl - D);
-    else c = 2 * Hk * D + g * G * D + (cl - 2 * D);
-    float wt[3], hist[3];
+  constexpr int NIT = (NCH + NT - 1) / NT;  // channels per thread
+  const bool has_z = p.z != nullptr;
+  auto chan = [&](int cl) {  // conv channel of group channel cl (q, k, then the G v heads)
+    if (cl < D) return g * D + cl;
+    if (cl < 2 * D) return Hk * D + g * D + (cl - D);
+    return 2 * Hk * D + g * G * D + (cl - 2 * D);
+  };
+  TA rw[NIT][4], rr3[NIT][3], rx[NIT][MAXR];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) wt[j] = (j < K - 1) ? ld(w, (size_t)c * K + j) : 0.0f;
-    const float wlast = ld(w, (size_t)c * K + K - 1);
+  for (int it = 0; it < NIT; ++it) {
+    const int c = chan(min(tid + it * NT, NCH - 1));
 #pragma unroll
-    for (int j = 0; j < 3; ++j) hist[j] = (j < K - 1) ? ld(ring, (size_t)j * C + c) : 0.0f;
-    for (int r = 0; r < nrows; ++r) {
-      const float xv = ld(x, (size_t)(r0 + r) * C + c);
-      float acc = 0.0f;
+    for (int jj = 0; jj < 4; ++jj) rw[it][jj] = w[(size_t)c * K + max(jj - (4 - K), 0)];  // tap for row t-3+jj
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < K - 1) acc += wt[j] * hist[j];
-      acc += wlast * xv;
-      s_qkv[r][cl] = silu(acc);
+    for (int jj = 0; jj < 3; ++jj) rr3[it][jj] = ring[(size_t)max(K - 4 + jj, 0) * C + c];  // row jj-3
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (j < K - 2) hist[j] = hist[j + 1];
-      if (K >= 2) {
-        if (K == 2) hist[0] = xv;
-        else if (K == 3) hist[1] = xv;
-        else hist[2] = xv;
-      }
+    for (int r = 0; r < MAXR; ++r) rx[it][r] = x[(size_t)(r0 + min(r, nrows - 1)) * C + c];
+  }
+  // gates of (row, value head) tid / G, tid % G; z and the norm weight of value
+  // channel tid of the group, for every row
+  const int gr = min(tid / G, MAXR - 1), gs = tid % G;
+  const float ga = p.a[(size_t)(r0 + min(gr, nrows - 1)) * Hv + g * G + gs];
+  const float gb = p.b[(size_t)(r0 + min(gr, nrows - 1)) * Hv + g * G + gs];
+  const TA *zp = has_z ? static_cast<const TA *>(p.z) : x;
+  const TA *nwp = has_z ? static_cast<const TA *>(p.norm_w) : x;
+  const int zc = min(tid, G * D - 1);
+  TA rz[MAXR];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r)
+    rz[r] = zp[has_z ? (size_t)(r0 + min(r, nrows - 1)) * Hv * D + (size_t)g * G * D + zc : 0];
+  const TA rnw = nwp[has_z ? zc % D : 0];
+
+  // ---- the state loads; the prologue's arithmetic hides their latency ---------
+  const int s = tid / kSlot, t = tid % kSlot;
+  const int h = g * G + s;
+  const int cq = t % CQ, rg = t / CQ;
+  const gptr<float> S_in = to_global(p.states[i]) + (size_t)h * D * D;  // table 0 / decode pointer
+  floatx4 st_reg[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr)
+    st_reg[rr] = *reinterpret_cast<const gptr<floatx4>>(S_in + (size_t)(rr * RG + rg) * D + 4 * cq);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- prologue: conv + SiLU of the group's channels for every row ----------
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int cl = tid + it * NT;
+    if (cl >= NCH) break;
+    const int c = chan(cl);
+    float wt[4], win[3];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) wt[jj] = (jj >= 4 - K) ? (float)rw[it][jj] : 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) win[jj] = (K - 4 + jj >= 0) ? (float)rr3[it][jj] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      if (r >= nrows) break;
+      const float xv = (float)rx[it][r];
+      s_qkv[r][cl] = silu(wt[0] * win[0] + wt[1] * win[1] + wt[2] * win[2] + wt[3] * xv);
+      win[0] = win[1];
+      win[1] = win[2];
+      win[2] = xv;
     }
-    if (MAXR == 1) {  // decode advances the conv state by one row
+    if (MAXR == 1) {  // decode advances the conv state by one row: new rows are t-2, t-1, t
 #pragma unroll
       for (int j = 0; j < 3; ++j)
-        if (j < K - 1) st(ring, (size_t)j * C + c, hist[j]);
+        if (j < K - 1) st(ring, (size_t)j * C + c, win[3 - (K - 1) + j]);
     }
   }
-  for (int e = tid; e < nrows * G; e += NT) {
-    const int r = e / G, ss = e - r * G;
-    s_a[r][ss] = p.a[(size_t)(r0 + r) * Hv + g * G + ss];
-    s_b[r][ss] = p.b[(size_t)(r0 + r) * Hv + g * G + ss];
+  if (tid < MAXR * G && gr < nrows) {
+    s_a[gr][gs] = ga;
+    s_b[gr][gs] = gb;
+  }
+  if (has_z && tid < G * D) {
+    const float nwv = (float)rnw;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r)
+      if (r < nrows) s_zw[r][tid] = silu((float)rz[r]) * nwv;
   }
   __syncthreads();
 
@@ -194,19 +242,18 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
     u.x = bv * (v.x - av * kv.x); u.y = bv * (v.y - av * kv.y);
     u.z = bv * (v.z - av * kv.z); u.w = bv * (v.w - av * kv.w);
 
-    float *dst;
-    if (MAXR == 1) dst = p.states[i];
-    else dst = (r < nrows - 1) ? p.states[(r + 1) * kTableSeqs + i] : p.states[i];
-    dst += (size_t)h * D * D;
+    gptr<float> dst = to_global(MAXR == 1 ? p.states[i]
+                                          : (r < nrows - 1) ? p.states[(r + 1) * kTableSeqs + i] : p.states[i]) +
+                      (size_t)h * D * D;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const int row = rr * RG + rg;
       const float kk = kh[row];
-      float4 nv;
+      floatx4 nv;
       nv.x = av * st_reg[rr].x + kk * u.x; nv.y = av * st_reg[rr].y + kk * u.y;
       nv.z = av * st_reg[rr].z + kk * u.z; nv.w = av * st_reg[rr].w + kk * u.w;
       st_reg[rr] = nv;
-      *reinterpret_cast<float4 *>(dst + (size_t)row * D + 4 * cq) = nv;
+      *reinterpret_cast<gptr<floatx4>>(dst + (size_t)row * D + 4 * cq) = nv;
     }
 
     if (rg == 0) {  // lanes 0..CQ-1 of the slot's first wave hold the head's outputs
@@ -215,18 +262,14 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
       o[0] = p.scale * (av * sq.x + qk * u.x); o[1] = p.scale * (av * sq.y + qk * u.y);
       o[2] = p.scale * (av * sq.z + qk * u.z); o[3] = p.scale * (av * sq.w + qk * u.w);
       const size_t obase = (size_t)(r0 + r) * Hv * D + (size_t)h * D + 4 * cq;
-      if (p.z != nullptr) {
+      if (has_z) {
         float ss2 = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
         ss2 = sum_within_span<CQ>(ss2);
         const float inv = 1.0f / sqrtf(ss2 / D + p.norm_eps);
-        const TA *zp = static_cast<const TA *>(p.z);
-        const TA *nw = static_cast<const TA *>(p.norm_w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = o[e] * inv * ld(nw, 4 * cq + e) * silu(ld(zp, obase + e));
+        const float4 zw = *reinterpret_cast<const float4 *>(&s_zw[r][s * D + 4 * cq]);
+        o[0] *= inv * zw.x; o[1] *= inv * zw.y; o[2] *= inv * zw.z; o[3] *= inv * zw.w;
       }
-      TO *out = static_cast<TO *>(p.out);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st(out, obase + e, o[e]);
+      store4(static_cast<TO *>(p.out) + obase, o);
     }
   }
 }
@@ -244,23 +287,21 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4)
   if (na < 1 || na > k) return;  // outside the caller's contract: sequence untouched
   if ((int)blockIdx.y < kCommitSplit) {
     if (na == k) return;  // table 0 already holds the last state
-    const float4 *src = reinterpret_cast<const float4 *>(p.tables[na * kTableSeqs + i]);
-    float4 *dst = reinterpret_cast<float4 *>(p.tables[i]);
+    // (native 4-float vectors: the struct-based float4 array ends up in scratch)
+    const gptr<const floatx4> src = to_global(reinterpret_cast<const floatx4 *>(p.tables[na * kTableSeqs + i]));
+    const gptr<floatx4> dst = to_global(reinterpret_cast<floatx4 *>(p.tables[i]));
     const int64_t per = (n4 + kCommitSplit - 1) / kCommitSplit;
     const int64_t beg = (int64_t)blockIdx.y * per, end = min(n4, beg + per);
-    for (int64_t i0 = beg + threadIdx.x; i0 < end; i0 += 256 * 8) {
-      float4 v[8];
+    // whole tiles of 256 x 8 float4 without conditions, then the tail
+    int64_t i0 = beg;
+    for (; i0 + 256 * 8 <= end; i0 += 256 * 8) {
+      floatx4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t idx = i0 + (int64_t)u * 256;
-        if (idx < end) v[u] = src[idx];
-      }
+      for (int u = 0; u < 8; ++u) v[u] = src[i0 + threadIdx.x + u * 256];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t idx = i0 + (int64_t)u * 256;
-        if (idx < end) dst[idx] = v[u];
-      }
+      for (int u = 0; u < 8; ++u) dst[i0 + threadIdx.x + u * 256] = v[u];
     }
+    for (int64_t idx = i0 + threadIdx.x; idx < end; idx += 256) dst[idx] = src[idx];
   } else {
     const int C = p.geo.conv_dim, R = p.geo.K - 1;
     const int c = ((int)blockIdx.y - kCommitSplit) * 256 + threadIdx.x;
@@ -269,11 +310,10 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4)
     const TE *x = static_cast<const TE *>(p.x) + (size_t)p.cu[i] * C;
     TE vals[3];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      if (r < R) {
-        const int idx = na + r;  // position in [old conv state ; accepted rows]
-        vals[r] = (idx < R) ? ring[(size_t)idx * C + c] : x[(size_t)(idx - R) * C + c];
-      }
+    for (int r = 0; r < 3; ++r) {  // position na + r of [old conv state ; accepted rows]
+      const int idx = na + min(r, R - 1);
+      const TE vr = ring[(size_t)min(idx, R - 1) * C + c], vx = x[(size_t)max(idx - R, 0) * C + c];
+      vals[r] = (idx < R) ? vr : vx;
     }
 #pragma unroll
     for (int r = 0; r < 3; ++r)
