@@ -32,7 +32,29 @@ __device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
 // float -> bf16 conversion rounds to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ void st(bf16 *p, size_t i, float v) { p[i] = (bf16)v; }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// x / (1 + e^-x), with the hardware reciprocal (about 1 ulp) instead of an IEEE
+// division (a dozen instructions); e^-x -> inf gives 0, e^-x -> 0 gives x.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+// 1 / sqrt(x) on the hardware (about 1 ulp); x > 0 here (an epsilon is added).
+__device__ __forceinline__ float rsqrt_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// One DPP lane move within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over each aligned group of N lanes (N = 1, 2, 4, 8 or 16), in every lane of the
+// group: swaps within pairs and quads, then the half-row and row mirrors (which pair
+// the two quads of an 8-lane half and the two halves of a 16-lane row).
+template <int N>
+__device__ __forceinline__ float sum_lanes(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "groups of up to 16 lanes");
+  if (N >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (N >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (N >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if (N >= 16) v += dpp_f<0x140>(v); // row_mirror
+  return v;
+}
 
 // Sum over all 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {

@@ -126,9 +126,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       ss += yv[e] * yv[e];
     }
     if (normalise) {
-#pragma unroll
-      for (int off = 1; off < TPH; off <<= 1) ss += __shfl_xor(ss, off);
-      const float inv = 1.0f / sqrtf(ss + p.l2_eps);
+      ss = sum_lanes<TPH>(ss);
+      const float inv = rsqrt_hw(ss + p.l2_eps);
 #pragma unroll
       for (int e = 0; e < 8; ++e) yv[e] *= inv;
     }
@@ -231,9 +230,8 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormLaunch p) {
   float ss = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += ov[e] * ov[e];
-#pragma unroll
-  for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off);
-  const float inv = 1.0f / sqrtf(ss / D + p.eps);
+  ss = sum_lanes<TPR>(ss);
+  const float inv = rsqrt_hw(ss / D + p.eps);
   float res[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) res[e] = ov[e] * inv * wv[e] * silu(zv[e]);

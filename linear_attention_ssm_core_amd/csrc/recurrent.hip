@@ -44,6 +44,9 @@ __device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
   *reinterpret_cast<uint2 *>(p) = w.u;
 }
 constexpr int kTableSeqs = 128;     // entries per WY pointer table
+// s_waitcnt immediate: vector-memory counter 0 (bits 3:0 and 15:14), expcnt and
+// lgkmcnt at their maxima (no wait)
+constexpr int kWaitVmem0 = (7 << 4) | (15 << 8);
 
 template <int D, int G, int MAXR, typename TA, typename TO>
 __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) {
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   __shared__ float s_a[MAXR][G], s_b[MAXR][G];
   __shared__ float s_qk[MAXR];
   __shared__ float s_zw[MAXR][G * D];  // silu(z) * norm weight of the group's value channels
+  __shared__ float *s_dst[MAXR];       // where the state after each row is stored
   __shared__ float4 s_red[2][G][4][CQ][2];
 
   const int Hk = p.geo.Hk, Hv = p.geo.Hv, K = p.geo.K, C = p.geo.conv_dim;
@@ -125,6 +129,9 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   const int gr = min(tid / G, MAXR - 1), gs = tid % G;
   const float ga = p.a[(size_t)(r0 + min(gr, nrows - 1)) * Hv + g * G + gs];
   const float gb = p.b[(size_t)(r0 + min(gr, nrows - 1)) * Hv + g * G + gs];
+  // destination of the state after row tid: table tid + 1, table 0 after the last
+  float *const dst_mid = p.states[(min(tid, max(nrows - 2, 0)) + (nrows > 1 ? 1 : 0)) * kTableSeqs + i];
+  float *const dst_last = p.states[i];
   const TA *zp = has_z ? static_cast<const TA *>(p.z) : x;
   const TA *nwp = has_z ? static_cast<const TA *>(p.norm_w) : x;
   const int zc = min(tid, G * D - 1);
@@ -175,6 +182,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
     s_a[gr][gs] = ga;
     s_b[gr][gs] = gb;
   }
+  if (tid < MAXR) s_dst[tid] = (MAXR > 1 && tid < nrows - 1) ? dst_mid : dst_last;
   if (has_z && tid < G * D) {
     const float nwv = (float)rnw;
 #pragma unroll
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
       sq = wave_sum(sq);
       sk = wave_sum(sk);
       dqk = wave_sum(dqk);
-      const float iq = 1.0f / sqrtf(sq + p.l2_eps), ik = 1.0f / sqrtf(sk + p.l2_eps);
+      const float iq = rsqrt_hw(sq + p.l2_eps), ik = rsqrt_hw(sk + p.l2_eps);
       for (int c = lane; c < D; c += kWave) {
         s_qkv[r][c] *= iq;
         s_qkv[r][D + c] *= ik;
@@ -208,6 +216,10 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   __syncthreads();
 
   // ---- the recurrence, row by row --------------------------------------------
+  // Every load is done by now (the state arrived during the prologue): the loop
+  // issues only stores, and no wait inside it makes a row wait for the previous
+  // row's state stores to complete.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   const int wv = t / kWave, lane = t % kWave;
   for (int r = 0; r < nrows; ++r) {
     const float *qh = &s_qkv[r][0];
@@ -242,9 +254,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
     u.x = bv * (v.x - av * kv.x); u.y = bv * (v.y - av * kv.y);
     u.z = bv * (v.z - av * kv.z); u.w = bv * (v.w - av * kv.w);
 
-    gptr<float> dst = to_global(MAXR == 1 ? p.states[i]
-                                          : (r < nrows - 1) ? p.states[(r + 1) * kTableSeqs + i] : p.states[i]) +
-                      (size_t)h * D * D;
+    gptr<float> dst = to_global(s_dst[r]) + (size_t)h * D * D;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const int row = rr * RG + rg;
@@ -265,7 +275,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
       if (has_z) {
         float ss2 = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
         ss2 = sum_within_span<CQ>(ss2);
-        const float inv = 1.0f / sqrtf(ss2 / D + p.norm_eps);
+        const float inv = rsqrt_hw(ss2 / D + p.norm_eps);
         const float4 zw = *reinterpret_cast<const float4 *>(&s_zw[r][s * D + 4 * cq]);
         o[0] *= inv * zw.x; o[1] *= inv * zw.y; o[2] *= inv * zw.z; o[3] *= inv * zw.w;
       }
