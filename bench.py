@@ -34,6 +34,36 @@ STATE_BYTES = HV * D * D * 4            # one sequence's fp32 state, 2 MiB
 CONV_DIM = 2 * HK * D + HV * D          # 8192
 
 
+# HBM traffic of one decode launch (recurrent_kernel<128,2,1>), from two rocprofv3
+# counter runs of `bench.py --steps 1 --warmup 0 --no-cpu-baseline` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, mean of the 100 decode dispatches), each scaled by
+# what the same counter reads for one 1 GiB device copy (`bench.py --copy-calib`:
+# FETCH_SIZE 524302.1 KiB, WRITE_SIZE 1048576.0 KiB per copy).  The figures hold for
+# the kernel sources they were taken on only (SHA-256 over the files below); for any
+# other source the traffic is reported as unknown.
+DECODE_TRAFFIC = {
+    "sources": ["linear_attention_ssm_core_amd/csrc/recurrent.hip", "linear_attention_ssm_core_amd/csrc/common.h",
+                "linear_attention_ssm_core_amd/csrc/internal.h"],
+    "sha256": "82cda49abff4ac52f58802336ab7f48e0b8ccea66adebd435b32ea85608c46e9",
+    "fetch_kib": 136027.8, "write_kib": 269312.0,
+    "fetch_scale": 1048576.0 / 524302.1, "write_scale": 1048576.0 / 1048576.0,
+}
+
+
+def decode_traffic_bytes():
+    """Measured HBM bytes of one decode launch, or None if the kernel has changed since."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in DECODE_TRAFFIC["sources"]:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != DECODE_TRAFFIC["sha256"]:
+        return None
+    t = DECODE_TRAFFIC
+    return (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024.0
+
+
 def decode_bytes_per_seq():
     """Algorithmic HBM bytes of one sequence-token of batched decode."""
     return (2 * STATE_BYTES            # state read + written
@@ -306,6 +336,7 @@ def main():
                    "hbm_frac": ver_bytes / (ver_ms / 1e3) / HBM_PEAK},
         "commit": {"ms": com_ms},
     }
+    dec_traffic = decode_traffic_bytes()
     line = {
         "metric": "GDN tokens/s: prefill (MFMA %) + batched decode/verify (HBM GB/s %), 1 GPU",
         "value": w.tokens_per_step / (ms_step / 1e3),
@@ -325,7 +356,9 @@ def main():
                    "verify_rows": w.v_rows},
         "roofline": {"bound": "hbm", "kernel": "gdn_decode_batched (recurrent_kernel<128,2,1>)",
                      "achieved": dec_gbs, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": dec_gbs * 1e9 / HBM_PEAK, "traffic": None,
+                     "frac": dec_gbs * 1e9 / HBM_PEAK,
+                     "traffic": None if dec_traffic is None else dec_traffic / (float(np.mean(dec_ms)) / 1e3) / 1e9,
+                     "traffic_bytes_per_launch": dec_traffic,
                      "bytes_per_launch": dec_bytes, "avg_launch_ms": float(np.mean(dec_ms)),
                      "launches_timed": int(dec_ms.size)},
         "phases": phases,

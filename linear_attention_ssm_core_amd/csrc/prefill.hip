@@ -24,20 +24,17 @@
 // MI355X design.  Three launches:
 //   1. chunk_table_kernel: chunk list of the packed batch (chunks restart at each
 //      sequence) and a longest-first sequence order.
-//   2. prep_kernel, one workgroup per (chunk, value head), all chunks in
-//      parallel: K K^T and Q K^T on bf16 MFMA, the 64x64 UT solve in fp32 (16x16
-//      blocks: the four diagonal blocks by substitution, the off-diagonal blocks
-//      by block substitution), then E and MT on MFMA.  E and MT go to the
-//      workspace as bf16 hi/lo pairs, already in the row order the next kernel
-//      loads as MFMA A operands.
-//   3. spine_kernel, one workgroup per (sequence, value head, 16-column block of
-//      d_v): the serial pass over the chunks.  Columns of h evolve independently,
-//      so a 128-wide state splits into 8 workgroups; the block's 128x16 state
-//      lives in MFMA accumulators, its bf16 hi/lo copy in LDS is the B operand of
-//      K h and Q h.  Each chunk is two MFMA stages separated by one barrier, and
-//      the next chunk's operands are loaded into registers while the current one
-//      computes.  The eight column blocks of a head are mapped onto one XCD so
-//      they share E/MT/K/Q through one L2.
+//   2. prep_kernel, one workgroup per (chunk, value head), all chunks in parallel: K K^T
+//      and Q K^T on bf16 MFMA, the 64x64 UT solve in fp32 (16x16 blocks: the four
+//      diagonal blocks by substitution, the off-diagonal blocks by block products),
+//      then E and MT on MFMA.  E and MT go to the workspace as bf16 hi/lo pairs in MFMA
+//      fragment order, so the next kernel loads each fragment as one contiguous 1 KiB
+//      block.
+//   3. spine_kernel, one workgroup per (sequence, value head, 32-column block of d_v):
+//      the serial pass over the chunks with specialised waves (K rows, Q rows, state
+//      owners); see the comment at the kernel.  Columns of h evolve independently, so a
+//      128-wide state splits into 4 workgroups, mapped onto one XCD so they share the
+//      head's operands through one L2.
 // Precision: fp32-derived operands (h, X, T, E, MT, and fp32 activations) enter
 // MFMA as bf16 hi + lo; a product takes hi*hi + hi*lo + lo*hi, about 2^-16
 // relative, which keeps states within 1e-4 of the fp64 recurrence.
