@@ -219,6 +219,22 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+def fill_bandwidth(torch, nbytes=1 << 30, reps=5):
+    """Attainable write-only bandwidth of a plain device fill (torch), GB/s."""
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.fill_(1)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.fill_(2)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del dst
+    return nbytes / (ms / 1e3) / 1e9
+
+
 def _event(torch):
     e = torch.cuda.Event(enable_timing=True)
     e.record(torch.cuda.current_stream())
@@ -362,8 +378,9 @@ def main():
                      "bytes_per_launch": dec_bytes, "avg_launch_ms": float(np.mean(dec_ms)),
                      "launches_timed": int(dec_ms.size)},
         "phases": phases,
-        "attainable": {"copy_gb_per_s": copy_bandwidth(torch),
-                       "note": "plain 1 GiB device-to-device copy (read + write bytes / time)"},
+        "attainable": {"copy_gb_per_s": copy_bandwidth(torch), "fill_gb_per_s": fill_bandwidth(torch),
+                       "note": "plain 1 GiB device-to-device copy (read + write bytes / time) and 1 GiB fill "
+                               "(bytes written / time)"},
         "wall_s_timed": t_wall,
     }
     if not args.no_cpu_baseline:
