@@ -205,13 +205,25 @@ __device__ __forceinline__ void store_tile(float *dst, int ld, const floatx4 &v,
   for (int rr = 0; rr < 4; ++rr) dst[(4 * lg + rr) * ld + lr] = sgn * v[rr];
 }
 
+// LDS of prep_kernel, three regions reused across its phases (41 KiB for bf16
+// activations, so three workgroups share a CU):
+//   R0  L^-1 (fp32, solve and the reads of T)       -> M hi/lo (bf16, MT products)
+//   R1  Abar (fp32, solve)                          -> K^T hi(/lo) (bf16, E products)
+//   R2  block-product scratch (solve), gates
+constexpr int kLF = 72;  // fp32 row stride of L^-1 and Abar
+template <int D, int NP>
+struct PrepLds {
+  static constexpr size_t r0 = (size_t)kC * kLF * 4 > (size_t)2 * kC * kLP * 2 ? (size_t)kC * kLF * 4 : (size_t)2 * kC * kLP * 2;
+  static constexpr size_t r1 = (size_t)kC * kLF * 4 > (size_t)NP * D * kLP * 2 ? (size_t)kC * kLF * 4 : (size_t)NP * D * kLP * 2;
+};
+
 template <int D, typename TY>
 __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, char *units) {
   constexpr bool SP = std::is_same<TY, float>::value;
   constexpr int NP = SP ? 2 : 1;
   constexpr int KS = D / 32;
   constexpr int NTI = D / 16;
-  constexpr int LF = kC + 1;  // fp32 LDS row stride
+  constexpr int NIG = D / 8 / 4;  // groups of 8 K columns staged per wave
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   const int cidx = blockIdx.x / Hv, h = blockIdx.x - cidx * Hv;
   const int seq = tb.chunk_seq[cidx];
@@ -231,14 +243,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   bf16 *MT_lo = MT_hi + kC * kC;
   float *Gam = reinterpret_cast<float *>(MT_lo + kC * kC);
 
+  using LDS = PrepLds<D, NP>;
+  __shared__ __align__(16) char s_r0[LDS::r0];
+  __shared__ __align__(16) char s_r1[LDS::r1];
+  __shared__ __align__(16) float s_Y[4][16][17];  // block-product scratch
   __shared__ float s_gam[kC], s_bb[kC], s_dec[kC];
-  __shared__ __align__(16) bf16 s_Kt[NP][D][kLP];    // K^T, B operand of E
-  __shared__ __align__(16) bf16 s_M[2][kC][kLP];     // M hi/lo, row-major
-  __shared__ __align__(16) float s_A[kC][LF];        // Abar (L = I + Abar), fp32
-  __shared__ __align__(16) float s_L[kC][LF];        // L^-1, fp32
-  __shared__ __align__(16) float s_Y[4][16][17];     // product scratch
+  float (*s_L)[kLF] = reinterpret_cast<float (*)[kLF]>(s_r0);
+  bf16 (*s_M)[kC][kLP] = reinterpret_cast<bf16 (*)[kC][kLP]>(s_r0);  // [2][kC][kLP]
+  float (*s_A)[kLF] = reinterpret_cast<float (*)[kLF]>(s_r1);
+  bf16 (*s_Kt)[D][kLP] = reinterpret_cast<bf16 (*)[D][kLP]>(s_r1);   // [NP][D][kLP]
 
-  // ---- A: gates; K^T staging and the phase-B fragments, all loads up front ----
+  // ---- A: gates; every load of the kernel up front ----
   if (wave == 0) {
     const size_t gi = (size_t)(t0 + min(lane, L - 1)) * Hv + h;
     const float a_raw = p.a[gi], b_raw = p.b[gi];
@@ -255,16 +270,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     s_dec[lane] = expf(glast - la);
     Gam[lane] = expf(la);
   }
-  constexpr int PER = kC * (D / 8) / 256;
-  bf16x8 kth[PER], ktl[PER];
+  // K rows for the K^T staging of phase D: lane = token, 8 consecutive columns
+  // per load (columns 8 (wave + 4 m) ..), written to LDS only once Abar is dead
+  bf16x8 kth[NIG], ktl[NIG];
 #pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int e = tid + 256 * m, sr = e / (D / 8), i0 = (e % (D / 8)) * 8;
-    frag8(Kb + (size_t)min(sr, L - 1) * CD + i0, kth[m], ktl[m]);
-  }
-  // wave w owns row block w of Q K^T -> M and of K K^T -> Abar
-  // (the wave's own K rows are loaded on their own: picking them out of kh by the
-  // wave index would be a run-time index into a register array, i.e. scratch memory)
+  for (int m = 0; m < NIG; ++m) frag8(Kb + (size_t)min(lane, L - 1) * CD + 8 * (wave + 4 * m), kth[m], ktl[m]);
+  // wave w owns row block w of Q K^T -> M and of K K^T -> Abar.  (Its own K rows
+  // are loaded on their own: picking them out of kh by the wave index would be a
+  // run-time index into a register array, i.e. scratch memory.)
   const int ti = wave;
   bf16x8 qh[KS], ql[KS], kih[KS], kil[KS], kh[4][KS], kl[4][KS];
   {
@@ -282,19 +295,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       for (int ks = 0; ks < KS; ++ks) frag8(krow + 32 * ks, kh[tj][ks], kl[tj][ks]);
     }
   }
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {  // rows past the chunk end are zero (E must see exact zeros)
-    const int e = tid + 256 * m, sr = e / (D / 8), i0 = (e % (D / 8)) * 8;
-    const bool live = sr < L;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      s_Kt[0][i0 + u][sr] = live ? kth[m][u] : (bf16)0.0f;
-      if (SP) s_Kt[NP - 1][i0 + u][sr] = live ? ktl[m][u] : (bf16)0.0f;
-    }
-  }
   __syncthreads();
 
-  // ---- B: Q K^T and K K^T for row block ti ----
+  // ---- B: Q K^T and K K^T for row block ti; M stays in registers until phase D ----
+  float mv[4][4];  // M[16 ti + 4 lg + rr][16 tj + lr]
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
     floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
@@ -310,28 +314,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       const int r = 16 * ti + 4 * lg + rr, c = 16 * tj + lr;
       const float dec = expf(s_gam[r] - s_gam[c]);
       s_A[r][c] = (c < r) ? s_bb[r] * dec * ak[rr] : 0.0f;
-      const float v = (c <= r) ? dec * aq[rr] : 0.0f;
-      bf16 hi, lo;
-      split_bf16(v, hi, lo);
-      s_M[0][r][c] = hi;
-      s_M[1][r][c] = lo;
+      mv[tj][rr] = (c <= r) ? dec * aq[rr] : 0.0f;
     }
   }
   __syncthreads();
 
   // ---- C: L^-1 for L = I + Abar (unit lower triangular), fp32 ----
-  // Level 1: the four 16x16 diagonal blocks by substitution (wave 0: lane =
-  // block * 16 + column); the other waves clear the upper blocks.
+  // Level 1: the four 16x16 diagonal blocks, right-looking substitution (wave 0:
+  // lane = block * 16 + column; after step m, x[m] is final and the updates of
+  // the rows below it are independent); the other waves clear the upper blocks.
   if (wave == 0) {
     const int bk = lane / 16, c = lane % 16;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == c) ? 1.0f : 0.0f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) acc -= s_A[16 * bk + r][16 * bk + m] * x[m];
-      x[r] = acc;
-    }
+    for (int m = 0; m < 15; ++m)
+#pragma unroll
+      for (int r = m + 1; r < 16; ++r) x[r] -= s_A[16 * bk + r][16 * bk + m] * x[m];
 #pragma unroll
     for (int r = 0; r < 16; ++r) s_L[16 * bk + r][16 * bk + c] = x[r];
   } else {
@@ -346,15 +346,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   if (wave < 2) {
     const int o = 32 * wave;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm16_f32(&s_A[o + 16][o], LF, &s_L[o][o], LF, acc, lr, lg);  // C A^-1
+    acc = mm16_f32(&s_A[o + 16][o], kLF, &s_L[o][o], kLF, acc, lr, lg);  // C A^-1
     store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
   }
   __syncthreads();
   if (wave < 2) {
     const int o = 32 * wave;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm16_f32(&s_L[o + 16][o + 16], LF, &s_Y[wave][0][0], 17, acc, lr, lg);  // B^-1 (C A^-1)
-    store_tile(&s_L[o + 16][o], LF, acc, -1.0f, lr, lg);
+    acc = mm16_f32(&s_L[o + 16][o + 16], kLF, &s_Y[wave][0][0], 17, acc, lr, lg);  // B^-1 (C A^-1)
+    store_tile(&s_L[o + 16][o], kLF, acc, -1.0f, lr, lg);
   }
   __syncthreads();
   // Level 3: the same identity with 32x32 blocks; wave w owns output tile (w/2, w%2).
@@ -362,7 +362,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     const int yi = wave >> 1, yj = wave & 1;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     // Y = C A^-1, C = Abar[32:64, 0:32], A^-1 = L^-1[0:32, 0:32] (lower: k >= yj)
-    for (int k = yj; k < 2; ++k) acc = mm16_f32(&s_A[32 + 16 * yi][16 * k], LF, &s_L[16 * k][16 * yj], LF, acc, lr, lg);
+    for (int k = yj; k < 2; ++k)
+      acc = mm16_f32(&s_A[32 + 16 * yi][16 * k], kLF, &s_L[16 * k][16 * yj], kLF, acc, lr, lg);
     store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
   }
   __syncthreads();
@@ -371,13 +372,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     // X = -B^-1 Y, B^-1 = L^-1[32:64, 32:64] (lower: k <= xi)
     for (int k = 0; k <= xi; ++k)
-      acc = mm16_f32(&s_L[32 + 16 * xi][32 + 16 * k], LF, &s_Y[2 * k + xj][0][0], 17, acc, lr, lg);
-    store_tile(&s_L[32 + 16 * xi][16 * xj], LF, acc, -1.0f, lr, lg);
+      acc = mm16_f32(&s_L[32 + 16 * xi][32 + 16 * k], kLF, &s_Y[2 * k + xj][0][0], 17, acc, lr, lg);
+    store_tile(&s_L[32 + 16 * xi][16 * xj], kLF, acc, -1.0f, lr, lg);
   }
   __syncthreads();
 
   // ---- D: T = L^-1 diag(b); MT = M T and E = K^T diag(D) T on MFMA ----
-  // Wave w owns rows j in [16w, 16w + 16) of T^T; its A operands are columns of T.
+  // Wave w owns rows j in [16w, 16w + 16) of T^T; its A operands are columns of T,
+  // read now, before L^-1's region is reused for M.
   const int jrow = 16 * wave + lr;
   const float bj = s_bb[jrow];
   bf16x8 th[2], tl[2], dh[2], dl[2];
@@ -396,6 +398,28 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       dl[ks][e] = lo;
     }
   }
+  __syncthreads();
+  // M (hi/lo) into R0, K^T (rows past the chunk end zero: E must see exact zeros) into R1
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      bf16 hi, lo;
+      split_bf16(mv[tj][rr], hi, lo);
+      s_M[0][16 * ti + 4 * lg + rr][16 * tj + lr] = hi;
+      s_M[1][16 * ti + 4 * lg + rr][16 * tj + lr] = lo;
+    }
+  {
+    const bool live = lane < L;
+#pragma unroll
+    for (int m = 0; m < NIG; ++m)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s_Kt[0][8 * (wave + 4 * m) + u][lane] = live ? kth[m][u] : (bf16)0.0f;
+        if (SP) s_Kt[NP - 1][8 * (wave + 4 * m) + u][lane] = live ? ktl[m][u] : (bf16)0.0f;
+      }
+  }
+  __syncthreads();
   // The lane's results below are X[r0 + lr][16 wave + 4 lg + r], r = 0..3 (X = MT or E,
   // r0 the tile's first row): k-offset 16 (wave & 1) + 4 lg + r within k-step wave / 2,
   // i.e. fragment lane fl, elements fe .. fe + 3.
