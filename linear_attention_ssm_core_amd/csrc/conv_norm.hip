@@ -71,11 +71,11 @@ struct Raw8<float> {
 // rows; every input row is read once with 16-byte loads (plus 3 history rows per
 // workgroup); a q or k head (d channels) is d/8 consecutive lanes, which reduce
 // its squared norm with shuffles.
-template <int D, typename TA, typename TY>
+template <int D, int K, typename TA, typename TY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void conv_l2norm_kernel(ConvLaunch p) {
   constexpr int TPH = D / 8;  // lanes per head
   constexpr int R = conv_rows<TA>();
-  const int C = p.geo.conv_dim, K = p.geo.K, Hk = p.geo.Hk;
+  const int C = p.geo.conv_dim, Hk = p.geo.Hk;
   const int c0 = (blockIdx.y * 256 + threadIdx.x) * 8;
   const bool active = c0 < C;  // uniform per head (C is a multiple of d)
   const int cc = active ? c0 : 0;
@@ -99,19 +99,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
   int seq_start = p.cu[seq], seq_end = p.cu[seq + 1];
 
-  // taps aligned to rows t-3 .. t: ws[jj] multiplies row t - 3 + jj (zero for the
-  // 4 - K rows before the window), so row offsets are compile-time constants
-  // (loaded unconditionally from a valid tap and zeroed after: a conditional load
-  // would be a branch with a wait for that load on every tap)
+  // The thread's 8 K taps are 8 K contiguous values: K 16-byte words (bf16).  They
+  // are loaded after the rows (the rows' latency is the one that matters) and
+  // aligned to rows t-3 .. t: ws[jj] multiplies row t - 3 + jj, zero for the 4 - K
+  // rows before the window.
+  Raw8<TA> wr[K];
+  auto load_w = [&]() {
+#pragma unroll
+    for (int q = 0; q < K; ++q) wr[q].load(w + (size_t)cc * K + 8 * q);
+  };
   float ws[4][8];
+  auto unpack_w = [&]() {
+    float wv[K][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
+    for (int q = 0; q < K; ++q) wr[q].get(wv[q]);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = jj - (4 - K);
-      const float v = ld(w, (size_t)(cc + e) * K + max(j, 0));
-      ws[jj][e] = (j >= 0) ? v : 0.0f;
-    }
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = jj - (4 - K), idx = e * K + (j < 0 ? 0 : j);
+        ws[jj][e] = (j >= 0) ? wv[idx / 8][idx % 8] : 0.0f;
+      }
+  };
 
   // conv + SiLU + L2 norm of row t from rows t-3 .. t (r[3] is row t)
   auto emit = [&](int64_t t, const float (&r)[4][8]) {
@@ -140,6 +149,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     Raw8<TA> xr[R + 3];  // rows t0 - 3 .. t1 - 1
 #pragma unroll
     for (int u = 0; u < R + 3; ++u) xr[u].load(x + (size_t)(t0 - 3 + u) * C + cc);
+    load_w();
+    unpack_w();
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       float r[4][8];
@@ -153,6 +164,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // General path (blocks at sequence starts, the ragged tail): row by row, with
   // rows t-3 .. t-1 of the current sequence in registers (from the conv state
   // before the sequence's first row; zero where no tap reaches).
+  load_w();
+  unpack_w();
   float r[4][8];
   auto load_win = [&](int64_t t) {
     // (through the global address space, so that its loads are not FLAT)
@@ -243,8 +256,22 @@ hipError_t conv_launch_y(const ConvLaunch &p, hipStream_t stream) {
   constexpr int R = conv_rows<TA>();
   const dim3 grid((unsigned)((p.T + R - 1) / R), (p.geo.conv_dim / 8 + 255) / 256), block(256);
   const bool y_bf16 = !p.y_f32 && p.geo.out_bf16;
-  if (y_bf16) hipLaunchKernelGGL((conv_l2norm_kernel<D, TA, bf16>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((conv_l2norm_kernel<D, TA, float>), grid, block, 0, stream, p);
+  // the conv width is a template parameter: the taps are then whole 16-byte words
+  // with compile-time positions
+  switch (p.geo.K) {
+    case 2:
+      if (y_bf16) hipLaunchKernelGGL((conv_l2norm_kernel<D, 2, TA, bf16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((conv_l2norm_kernel<D, 2, TA, float>), grid, block, 0, stream, p);
+      break;
+    case 3:
+      if (y_bf16) hipLaunchKernelGGL((conv_l2norm_kernel<D, 3, TA, bf16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((conv_l2norm_kernel<D, 3, TA, float>), grid, block, 0, stream, p);
+      break;
+    default:
+      if (y_bf16) hipLaunchKernelGGL((conv_l2norm_kernel<D, 4, TA, bf16>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((conv_l2norm_kernel<D, 4, TA, float>), grid, block, 0, stream, p);
+      break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid2((p.geo.conv_dim + 255) / 256, p.n);
