@@ -28,6 +28,10 @@ def _conv_case(d, y_dtype):
     ([64], W.TINY_DIMS, "f32"),
     ([4096], W.QWEN_DIMS, "bf16"),
     ([1, 0, 2, 3, 700, 65, 0, 129], W.QWEN_DIMS, "bf16"),   # shorter than K-1, empty, ragged
+    # conv widths 2 and 3 (the kernel is specialised per width): blocks wholly inside
+    # a sequence, blocks at sequence starts, short and empty sequences
+    ([100, 0, 37, 64, 5, 1], W.Dims(Hk=2, Hv=4, dk=32, dv=32, K=2), "f32"),
+    ([100, 0, 37, 64, 5, 2], W.Dims(Hk=2, Hv=4, dk=64, dv=64, K=3), "bf16"),
 ])
 def test_conv_l2norm(lens, dims, act):
     d = W.prefill_inputs(4000 + len(lens), lens, dims, act=act)

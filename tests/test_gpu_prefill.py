@@ -110,6 +110,17 @@ def test_prefill_ragged_and_empty(dims, act):
     assert np.array_equal(ds.h_host()[4], d["S0"][4])  # the empty sequence keeps its state
 
 
+@pytest.mark.parametrize("dims,act,n,heads", [(W.TINY_DIMS, "f32", 200, None),
+                                              (W.QWEN_DIMS, "bf16", 40, [0, 17, 31])])
+def test_prefill_many_short_sequences(dims, act, n, heads):
+    """Batches of many short sequences (0..150 rows): the chunk table, the
+    longest-first order and one spine workgroup set per sequence."""
+    lens = np.random.default_rng(4321 + n).integers(0, 151, size=n)
+    d = W.prefill_inputs(5000 + n, list(lens), dims, act=act)
+    out, ds, y = _run(d, fused=False, epilogue=False, y_dtype=torch.float32)
+    _check(d, out, ds, _ref(d, y=host(y), heads=heads), heads=heads, check_ring=False)
+
+
 def test_prefill_resume_equals_one_call():
     """Prefill of rows [0, 100) then [100, 300) with the carried state equals one
     call over [0, 300) (states and conv states resume through the same buffers)."""

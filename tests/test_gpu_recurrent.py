@@ -33,10 +33,12 @@ def _decode_ref(d, step, S, ring, idx, with_norm=True, scale=1.0):
     return (r["out"] if with_norm else r["o"]), r["S"], r["ring"]
 
 
-@pytest.mark.parametrize("with_norm", [False, True])
-def test_decode_tiny_fp32(with_norm):
-    """d = 32, 2 key / 4 value heads, fp32 everything, random states, 5 steps."""
-    d = W.decode_inputs(2000, 3, 5, W.TINY_DIMS, act="f32")
+@pytest.mark.parametrize("with_norm,K", [(False, 4), (True, 4), (True, 2), (True, 3)])
+def test_decode_tiny_fp32(with_norm, K):
+    """d = 32, 2 key / 4 value heads, fp32 everything, random states, 5 steps;
+    conv widths 2, 3 and 4."""
+    dims = W.Dims(Hk=2, Hv=4, dk=32, dv=32, K=K)
+    d = W.decode_inputs(2000 + K, 3, 5, dims, act="f32")
     ds = DeviceStates(d["S0"], d["ring"], torch.float32)
     S, ring = d["S0"].astype(np.float64), d["ring"].astype(np.float64)
     idx = np.arange(3)
@@ -126,13 +128,16 @@ def _verify_gpu(d, ds, tab, out_dtype=torch.float32, with_norm=True):
     return out
 
 
-@pytest.mark.parametrize("case", ["config3", "tiny_fp32", "edge_k"])
+@pytest.mark.parametrize("case", ["config3", "tiny_fp32", "tiny_k3", "edge_k"])
 def test_verify_and_commit(case):
     if case == "config3":
         d = W.config(3)
         sample = np.array([0, 3, 11, 31, 47, 63])
     elif case == "tiny_fp32":
         d = W.verify_inputs(3001, 5, W.TINY_DIMS, act="f32")
+        sample = np.arange(5)
+    elif case == "tiny_k3":  # conv width 3, bf16
+        d = W.verify_inputs(3003, 5, W.Dims(Hk=2, Hv=4, dk=32, dv=32, K=3), act="bf16")
         sample = np.arange(5)
     else:  # k = 1, 2 and 16, and the widest batch (128 sequences)
         ks = np.array(([1, 2, 16] * 43)[:128])
