@@ -151,12 +151,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int u = 0; u < R + 3; ++u) xr[u].load(x + (size_t)(t0 - 3 + u) * C + cc);
     load_w();
     unpack_w();
+    // sliding window of widened rows: each raw row is widened once
+    float r[4][8];
+#pragma unroll
+    for (int jj = 0; jj < 3; ++jj) xr[jj].get(r[jj]);
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      float r[4][8];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) xr[u + jj].get(r[jj]);
+      xr[u + 3].get(r[3]);
       emit(t0 + u, r);
+#pragma unroll
+      for (int jj = 0; jj < 3; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[jj][e] = r[jj + 1][e];
     }
     return;
   }
