@@ -29,7 +29,18 @@
  *    `nv * kd * vd` per-sequence state order of the `h_state_bytes` field.
  *  - Z-gated RMSNorm per (token, value head) over d_v (handles
  *    `gated_rms_norm_k`, `gated_rms_norm_prefill_k`):
- *        out = o / sqrt(mean(o^2) + eps) * w * SiLU(z).
+ *        out = o / sqrt(mean(o^2) + eps) * w * SiLU(z),
+ *    or with the gate sigmoid(z) in place of SiLU(z) for a model of the
+ *    `gdn_norm_sigmoid` kind (doc comment of `gated_rms_norm_f32_strided_k`).
+ *  - Optional storage of the state in IEEE binary16 (the FP16 h-state variants
+ *    and the `ssm_h_f16_to_f32_k` / `ssm_h_f32_to_f16_k` width converters on
+ *    the layer_struct.rs page): the state is rounded to the nearest binary16
+ *    value (ties to even) whenever it is stored -- after every token for the
+ *    one-token and verify forms, once at the end for a prefill, which widens
+ *    the stored state, runs at full width and narrows the result.
+ *  - Optional record of the rank-1 update vector u_t of every token (what a
+ *    write-on-accept verify keeps instead of whole states; `gdn_wy4_woa_k`,
+ *    `gdn_wy4_fold_k` on the layer_struct.rs page).
  *
  * Value head h reads key head floor(h * Hk / Hv) (grouped heads).
  * All arithmetic is double precision, in the order the definitions state.
@@ -44,6 +55,25 @@
 #endif
 
 static double silu(double x) { return x / (1.0 + exp(-x)); }
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* Nearest IEEE binary16 value of x, ties to even (the default rounding mode of
+ * nearbyint): 11 significant bits, so the spacing of values in [2^(e-1), 2^e) is
+ * 2^(e-11), never below the subnormal spacing 2^-24; beyond the largest finite
+ * value 65504 the result overflows to infinity. */
+double orc_round_binary16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  frexp(x, &e);
+  int q = e - 11;
+  if (q < -24) q = -24;
+  const double r = ldexp(nearbyint(ldexp(x, -q)), q);
+  return fabs(r) > 65504.0 ? copysign(INFINITY, x) : r;
+}
+
+void orc_round_binary16_array(double *x, long long n) {
+  for (long long i = 0; i < n; ++i) x[i] = orc_round_binary16(x[i]);
+}
 
 int orc_num_threads(void) {
 #ifdef _OPENMP
@@ -126,12 +156,18 @@ void orc_conv_l2norm(int n, const int32_t *cu, int Hk, int Hv, int dk, int dv, i
  *   heads [nh]          value heads to compute (NULL: all heads, nh ignored)
  *   states_out          NULL, or [T][nh][dk][dv]: h after every token, for the
  *                        listed heads in list order
+ *   state_round         0: full width throughout; 1: the state is rounded to
+ *                        binary16 after every token (the output of the token
+ *                        uses the state before that rounding); 2: only the final
+ *                        state of each sequence is rounded
+ *   u_out               NULL, or [T][nh][dv]: the update vector u of every token
  * Heads not listed are left untouched in S and o.
  */
 void orc_delta_rule(int n, const int32_t *cu, int Hk, int Hv, int dk, int dv,
                     const double *q, const double *k, const double *v, const double *a,
                     const double *b, double scale, double *S, double *o,
-                    const int32_t *heads, int nh, double *states_out) {
+                    const int32_t *heads, int nh, double *states_out, int state_round,
+                    double *u_out) {
   if (heads == NULL) nh = Hv;
   const long long pairs = (long long)n * nh;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -162,8 +198,11 @@ void orc_delta_rule(int n, const int32_t *cu, int Hk, int Hv, int dk, int dv,
         for (int i = 0; i < dk; ++i) acc += qt[i] * hs[(size_t)i * dv + j];
         ot[j] = scale * acc;
       }
+      if (state_round == 1 || (state_round == 2 && t == cu[s + 1] - 1))
+        for (size_t e = 0; e < (size_t)dk * dv; ++e) hs[e] = orc_round_binary16(hs[e]);
       if (states_out)
         memcpy(states_out + ((size_t)t * nh + hi) * (size_t)dk * dv, hs, sizeof(double) * (size_t)dk * dv);
+      if (u_out) memcpy(u_out + ((size_t)t * nh + hi) * (size_t)dv, u, sizeof(double) * (size_t)dv);
     }
     free(kv);
     free(u);
@@ -173,9 +212,10 @@ void orc_delta_rule(int n, const int32_t *cu, int Hk, int Hv, int dk, int dv,
 /*
  * Z-gated RMSNorm per (token, value head) over dv.
  *   o, z, out [T][Hv][dv];  w [dv] shared by all heads.
+ *   gate_sigmoid: 0 gates with SiLU(z), 1 with sigmoid(z).
  */
 void orc_gated_rmsnorm(long long T, int Hv, int dv, const double *o, const double *z,
-                       const double *w, double eps, double *out) {
+                       const double *w, double eps, int gate_sigmoid, double *out) {
 #pragma omp parallel for schedule(static)
   for (long long r = 0; r < T * Hv; ++r) {
     const double *orow = o + (size_t)r * dv;
@@ -184,6 +224,7 @@ void orc_gated_rmsnorm(long long T, int Hv, int dv, const double *o, const doubl
     double ss = 0.0;
     for (int j = 0; j < dv; ++j) ss += orow[j] * orow[j];
     double inv = 1.0 / sqrt(ss / dv + eps);
-    for (int j = 0; j < dv; ++j) dst[j] = orow[j] * inv * w[j] * silu(zrow[j]);
+    for (int j = 0; j < dv; ++j)
+      dst[j] = orow[j] * inv * w[j] * (gate_sigmoid ? sigmoid(zrow[j]) : silu(zrow[j]));
   }
 }

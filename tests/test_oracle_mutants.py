@@ -12,6 +12,7 @@ import pytest
 import oracle
 from oracle import build as obuild
 from tests import test_oracle_pins as P
+from tests import test_oracle_pins_variants as V
 
 MUTANTS = {
     "drop_decay_in_update": ("hs[(size_t)i * dv + j] = at * hs[(size_t)i * dv + j]",
@@ -28,7 +29,14 @@ MUTANTS = {
     "conv_state_not_advanced": ("memcpy(rs, tmp, sizeof(double) * (size_t)R * C);", "(void)tmp;"),
     "l2_eps_outside_sqrt": ("1.0 / sqrt(ss + l2_eps)", "1.0 / (sqrt(ss) + l2_eps)"),
     "rmsnorm_sum_not_mean": ("sqrt(ss / dv + eps)", "sqrt(ss + eps)"),
-    "gate_sigmoid_not_silu": ("* w[j] * silu(zrow[j])", "* w[j] / (1.0 + exp(-zrow[j]))"),
+    "gate_sigmoid_not_silu": (": silu(zrow[j]))", ": sigmoid(zrow[j]))"),
+    "sigmoid_gate_is_silu": ("(gate_sigmoid ? sigmoid(zrow[j])", "(gate_sigmoid ? silu(zrow[j])"),
+    "binary16_ties_away_from_zero": ("ldexp(nearbyint(ldexp(x, -q)), q)", "ldexp(round(ldexp(x, -q)), q)"),
+    "binary16_one_bit_short": ("int q = e - 11;", "int q = e - 10;"),
+    "binary16_no_subnormal_floor": ("if (q < -24) q = -24;", "(void)0;"),
+    "f16_state_never_rounded": ("if (state_round == 1 ||", "if (state_round == 9 ||"),
+    "u_record_holds_kv": ("memcpy(u_out + ((size_t)t * nh + hi) * (size_t)dv, u,",
+                          "memcpy(u_out + ((size_t)t * nh + hi) * (size_t)dv, kv,"),
 }
 
 BATTERY = [
@@ -46,6 +54,13 @@ BATTERY = [
     P.test_l2_norm_value,
     P.test_gated_rmsnorm_library_and_closed_form,
     P.test_verify_intermediates_equal_decode_steps_and_commit,
+    V.test_round_binary16_matches_numpy_float16,
+    V.test_f16_state_is_rounded_where_it_is_stored,
+    V.test_f16_every_token_equals_step_by_step_numpy_half,
+    V.test_sigmoid_gated_norm_library_and_closed_form,
+    V.test_woa_stash_u_equals_exact_rank1_update,
+    lambda: V.test_fold_of_stash_equals_recorded_states("f16"),
+    V.test_decode_tokens_equals_chunked_form_and_single_decodes,
 ]
 
 
