@@ -42,8 +42,9 @@ CONV_DIM = 2 * HK * D + HV * D          # 8192
 # the kernel sources they were taken on only (SHA-256 over the files below); for any
 # other source the traffic is reported as unknown.
 DECODE_TRAFFIC = {
-    "sources": ["linear_attention_ssm_core_amd/csrc/recurrent.hip", "linear_attention_ssm_core_amd/csrc/common.h",
-                "linear_attention_ssm_core_amd/csrc/internal.h"],
+    "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
+                "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
+                "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
     "sha256": "82cda49abff4ac52f58802336ab7f48e0b8ccea66adebd435b32ea85608c46e9",
     "fetch_kib": 136027.8, "write_kib": 269312.0,
     "fetch_scale": 1048576.0 / 524302.1, "write_scale": 1048576.0 / 1048576.0,
@@ -78,6 +79,33 @@ def verify_bytes(ks):
     per_seq = STATE_BYTES * (1 + ks) + 3 * CONV_DIM * 2
     per_row = CONV_DIM * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4
     return int(np.sum(per_seq) + per_row * np.sum(ks)) + CONV_DIM * 4 * 2
+
+
+def stash_row_bytes():
+    """One write-on-accept stash row: k_hat of every key head, u and a of every value head."""
+    return ((HK * D + HV * D + HV + 3) // 4 * 4) * 4
+
+
+def woa_verify_bytes(ks):
+    """Write-on-accept verify: one state read per sequence, the stash row of every row."""
+    per_seq = STATE_BYTES + 3 * CONV_DIM * 2
+    per_row = CONV_DIM * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4 + stash_row_bytes()
+    return int(len(ks) * per_seq + per_row * np.sum(ks)) + CONV_DIM * 4 * 2
+
+
+def fold_bytes(n_acc):
+    """Fold: every state read and written once, the accepted stash rows read, the
+    conv state rebuilt from the accepted rows."""
+    per_seq = 2 * STATE_BYTES + 2 * 3 * CONV_DIM * 2
+    return int(len(n_acc) * per_seq + np.sum(n_acc) * (stash_row_bytes() + CONV_DIM * 2))
+
+
+def tokens_bytes(ks, state_bytes=None):
+    """k consecutive tokens per sequence: the state read and written once."""
+    sb = STATE_BYTES if state_bytes is None else state_bytes
+    per_seq = 2 * sb + 2 * 3 * CONV_DIM * 2
+    per_row = CONV_DIM * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4
+    return int(len(ks) * per_seq + per_row * np.sum(ks)) + CONV_DIM * 4 * 2
 
 
 def prefill_flops_per_token():
@@ -202,6 +230,78 @@ def run_step(torch, B, w, ev=None):
     rec("v1")
     B.gdn_verify_commit(w.v_x, w.v_rp, w.v_tab, w.v_cu, w.v_nacc, dims)
     rec("v2")
+
+
+def _timed(torch, fn, reps):
+    """Mean duration (ms) of fn() over reps back-to-back calls, one event pair
+    on the launch stream, after one untimed call."""
+    fn()
+    a, b = _event(torch), None
+    for _ in range(reps):
+        fn()
+    b = _event(torch)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def variant_phases(torch, B, W, w, reps=10):
+    """The variant forms on the step's workloads, timed outside the step on
+    buffers of their own: write-on-accept verify + fold, binary16-state decode,
+    the k-token decode, and decode with raw gates and the sigmoid-gated norm."""
+    dev, bf, f32, f16 = "cuda", torch.bfloat16, torch.float32, torch.float16
+    dims = w.dims
+    res = {}
+    v = W.config(3)
+    h = [torch.from_numpy(v["S0"][i]).to(f32).to(dev) for i in range(w.v_n)]
+    hp = B.ptr_array(h)
+    ring = [torch.from_numpy(v["ring"][i]).to(bf).to(dev) for i in range(w.v_n)]
+    rp = B.ptr_array(ring)
+    stash = torch.empty(max(B.gdn_woa_stash_bytes(w.v_x, w.v_cu, w.v_maxk, w.v_out, dims) // 4, 1),
+                        dtype=f32, device=dev)
+    woa = lambda: B.gdn_verify_woa(w.v_x, w.v_w, rp, w.v_a, w.v_b, hp, w.v_cu, w.v_maxk, w.v_out, dims,
+                                   stash=stash, z=w.v_z, norm_w=w.v_nw)
+    fold = lambda: B.gdn_fold_accepted(w.v_x, rp, hp, stash, w.v_cu, w.v_nacc, dims)
+    ms_v, ms_f = _timed(torch, woa, reps), _timed(torch, fold, reps)
+    vb, fb = woa_verify_bytes(w.v_ks), fold_bytes(v["n_acc"])
+    res["verify_woa"] = {"rows": w.v_rows, "ms": ms_v, "fold_ms": ms_f, "tokens_per_s": w.v_rows / (ms_v / 1e3),
+                         "gb_per_s": vb / (ms_v / 1e3) / 1e9, "hbm_frac": vb / (ms_v / 1e3) / HBM_PEAK,
+                         "fold_gb_per_s": fb / (ms_f / 1e3) / 1e9, "fold_hbm_frac": fb / (ms_f / 1e3) / HBM_PEAK,
+                         "bytes": vb, "fold_bytes": fb}
+    # k consecutive tokens per sequence on the verify's rows (state written once)
+    toks = lambda: B.gdn_decode_tokens(w.v_x, w.v_w, rp, w.v_a, w.v_b, hp, w.v_cu, w.v_maxk, w.v_out, dims,
+                                       z=w.v_z, norm_w=w.v_nw)
+    ms_t = _timed(torch, toks, reps)
+    tb = tokens_bytes(w.v_ks)
+    res["decode_tokens"] = {"rows": w.v_rows, "ms": ms_t, "tokens_per_s": w.v_rows / (ms_t / 1e3),
+                            "gb_per_s": tb / (ms_t / 1e3) / 1e9, "hbm_frac": tb / (ms_t / 1e3) / HBM_PEAK}
+    del h, stash
+    # binary16 states: the decode workload, 100 steps
+    d = W.config(2)
+    h16 = [torch.from_numpy(d["S0"][i]).to(f16).to(dev) for i in range(w.d_n)]
+    hp16 = B.ptr_array(h16)
+    opt16 = B.options(f16)
+
+    def dec16():
+        for s_ in range(w.d_steps):
+            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp, w.d_a[s_], w.d_b[s_], hp16, w.d_out, dims,
+                                 z=w.d_z[s_], norm_w=w.d_nw, opt=opt16)
+    ms16 = _timed(torch, dec16, 1) / w.d_steps
+    db16 = w.d_n * (decode_bytes_per_seq() - STATE_BYTES) + CONV_DIM * 4 * 2 + D * 2
+    res["decode_f16_state"] = {"ms_per_launch": ms16, "tokens_per_s": w.d_n / (ms16 / 1e3),
+                               "gb_per_s": db16 / (ms16 / 1e3) / 1e9, "hbm_frac": db16 / (ms16 / 1e3) / HBM_PEAK}
+    del h16
+    # raw gate inputs and the sigmoid-gated norm (the fp32-state decode otherwise)
+    optg = B.options(None, gates="raw", norm_gate="sigmoid")
+
+    def decg():
+        for s_ in range(w.d_steps):
+            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp, w.d_a[s_], w.d_b[s_], w.d_hp, w.d_out, dims,
+                                 z=w.d_z[s_], norm_w=w.d_nw, opt=optg)
+    msg = _timed(torch, decg, 1) / w.d_steps
+    db = w.d_n * decode_bytes_per_seq() + CONV_DIM * 4 * 2 + D * 2
+    res["decode_raw_gates_sigmoid_norm"] = {"ms_per_launch": msg, "gb_per_s": db / (msg / 1e3) / 1e9,
+                                            "hbm_frac": db / (msg / 1e3) / HBM_PEAK}
+    return res
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
@@ -381,6 +481,7 @@ def main():
                      "bytes_per_launch": dec_bytes, "avg_launch_ms": float(np.mean(dec_ms)),
                      "launches_timed": int(dec_ms.size) * w.d_steps},
         "phases": phases,
+        "variants": variant_phases(torch, B, W, w),
         "attainable": {"copy_gb_per_s": copy_bandwidth(torch), "fill_gb_per_s": fill_bandwidth(torch),
                        "note": "plain 1 GiB device-to-device copy (read + write bytes / time) and 1 GiB fill "
                                "(bytes written / time)"},

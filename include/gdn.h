@@ -14,6 +14,11 @@
  *        - k draft rows per sequence that records every intermediate state through
  *          the WY pointer tables, and the commit of the accepted prefix
  *                                                      -> gdn_verify_multi, gdn_verify_commit
+ *        - the write-on-accept verify, which stores per-row update vectors instead
+ *          of states, and the fold of the accepted rows into the state
+ *                                                      -> gdn_verify_woa, gdn_fold_accepted
+ *        - k consecutive tokens for each of many sequences, state written once
+ *                                                      -> gdn_decode_tokens
  *   3. Z-gated RMSNorm  out = o / sqrt(mean(o^2) + eps) * w * SiLU(z)
  *                                                      -> gdn_gated_rmsnorm
  *
@@ -43,12 +48,23 @@
  *     conv_dim = 2*H_k*d_k + H_v*d_v.  Value head h reads key head h / (H_v/H_k).
  *   - Activation rows are packed [q (H_k*d_k) | k (H_k*d_k) | v (H_v*d_v)],
  *     head-major inside each block, row stride conv_dim elements.
- *   - The recurrent state of a sequence is fp32 h[H_v][d_k][d_v] = S^T per value
- *     head (d_v fastest), reached through a device array of per-sequence pointers.
+ *   - The recurrent state of a sequence is h[H_v][d_k][d_v] = S^T per value head
+ *     (d_v fastest), fp32 by default or IEEE binary16 (gdn_options.state_dtype),
+ *     reached through a device array of per-sequence pointers.  All recurrence
+ *     arithmetic is fp32; a binary16 state is widened when read and rounded to
+ *     nearest-even when stored (FP16 h-state variants and the ssm_h_f16_to_f32_k /
+ *     ssm_h_f32_to_f16_k converters, layer_struct.rs page).
  *     The conv state of a sequence is its last (K-1) raw pre-conv rows, oldest
  *     first, [K-1][conv_dim] in the activation dtype, also through a pointer array.
- *   - a, b are fp32 [rows][H_v]; z is [rows][H_v*d_v]; norm_w is [d_v], shared by
- *     all heads; z and norm_w use the activation dtype.
+ *   - a, b are fp32 [rows][H_v]: the decay and write strength, or, with
+ *     gdn_options.gate_mode = GDN_GATES_RAW, the raw gate inputs g and beta from
+ *     which the kernels form a = exp(-softplus(g)) and b = sigmoid(beta) (the
+ *     ba_gates / compute_gdn_gates handles of the layer_struct.rs page name this
+ *     step; the pages give no formula, this is the plainest one).
+ *   - z is [rows][H_v*d_v]; norm_w is [d_v], shared by all heads; z and norm_w use
+ *     the activation dtype.  The norm gate is SiLU(z), or sigmoid(z) with
+ *     gdn_options.norm_gate = GDN_NORM_GATE_SIGMOID (a gdn_norm_sigmoid model,
+ *     doc comment of gated_rms_norm_f32_strided_k on the layer_struct.rs page).
  *   - Errors: any status other than GDN_OK except GDN_ERR_HIP means nothing was
  *     launched.  GDN_ERR_HIP reports a launch failure (hipGetLastError).
  *   - Calls on one stream are ordered; state buffers must not be shared by calls
@@ -64,7 +80,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 /* Batched-verify pointer-table layout: per layer, 16 tables of 128 u64 entries
  * back to back.  Table 0 holds each sequence's state, table t+1 its state after
@@ -79,6 +95,10 @@ extern "C" {
 /* Chunk length of the chunked prefill (tokens). */
 #define GDN_PREFILL_CHUNK 64
 
+/* Most tokens per sequence in one gdn_decode_tokens call (16 drafts plus one; the
+ * K = 17 gated_delta_rule_wy17 handle, layer_struct.rs page). */
+#define GDN_DECODE_MAX_TOKENS 17
+
 typedef enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_INVALID_ARG = 1, /* NULL required pointer, bad sizes, struct_size mismatch   */
@@ -89,8 +109,32 @@ typedef enum gdn_status {
 
 typedef enum gdn_dtype {
   GDN_DTYPE_F32 = 0,
-  GDN_DTYPE_BF16 = 1
+  GDN_DTYPE_BF16 = 1,
+  GDN_DTYPE_F16 = 2  /* IEEE binary16: recurrent states only (gdn_options.state_dtype) */
 } gdn_dtype;
+
+typedef enum gdn_gate_mode {
+  GDN_GATES_DIRECT = 0, /* a = decay a_t in [0, 1], b = write strength b_t           */
+  GDN_GATES_RAW = 1     /* a = g, b = beta; a_t = exp(-softplus(g)), b_t = sigmoid(beta) */
+} gdn_gate_mode;
+
+typedef enum gdn_norm_gate {
+  GDN_NORM_GATE_SILU = 0,   /* out = rmsnorm(o) * w * SiLU(z)    */
+  GDN_NORM_GATE_SIGMOID = 1 /* out = rmsnorm(o) * w * sigmoid(z) */
+} gdn_norm_gate;
+
+/* Options of the recurrence and norm entry points, the last member of their
+ * argument structs.  All zero = fp32 states, direct gates, SiLU norm gate.  An
+ * entry point refuses (GDN_ERR_INVALID_ARG) a non-zero option it does not take:
+ * gdn_verify_commit and gdn_fold_accepted take only state_dtype,
+ * gdn_gated_rmsnorm only norm_gate. */
+typedef struct gdn_options {
+  int32_t state_dtype; /* GDN_DTYPE_F32 or GDN_DTYPE_F16: element type of every
+                          recurrent state the call reads or writes              */
+  int32_t gate_mode;   /* gdn_gate_mode                                         */
+  int32_t norm_gate;   /* gdn_norm_gate (fused or standalone gated norm)        */
+  int32_t reserved;    /* must be 0                                             */
+} gdn_options;
 
 /* Head geometry.  Supported: d_k == d_v in {32, 64, 128}; H_v / H_k in {1, 2, 4};
  * conv_kernel (taps K) in {2, 3, 4}. */
@@ -161,7 +205,7 @@ typedef struct gdn_prefill_args {
   void *const *conv_state;     /* [n] pointers (with x), in/out                  */
   const float *a;              /* [T][H_v] decay a_t in [0, 1]                   */
   const float *b;              /* [T][H_v] write strength b_t                    */
-  float *const *h_state;       /* [n] pointers to fp32 [H_v][d_k][d_v], in/out    */
+  void *const *h_state;        /* [n] pointers to [H_v][d_k][d_v] states, in/out  */
   const void *z;               /* [T][H_v*d_v] or NULL                          */
   const void *norm_w;          /* [d_v] (with z)                                */
   void *out;                   /* [T][H_v*d_v]                                  */
@@ -171,6 +215,9 @@ typedef struct gdn_prefill_args {
   float reserved_f;            /* must be 0                                     */
   void *workspace;             /* device scratch, >= required bytes             */
   size_t workspace_bytes;
+  gdn_options opt;             /* state dtype (the stored state is widened at a
+                                  sequence's start and narrowed at its end), gate
+                                  mode, norm gate of the epilogue                 */
 } gdn_prefill_args;
 
 /* Workspace bytes gdn_prefill_chunked needs for these arguments (pointers are not
@@ -200,7 +247,7 @@ typedef struct gdn_decode_args {
   void *const *conv_state;     /* [n] pointers, in/out                          */
   const float *a;              /* [n][H_v]                                      */
   const float *b;              /* [n][H_v]                                      */
-  float *const *h_state;       /* [n] pointers to fp32 [H_v][d_k][d_v], in/out    */
+  void *const *h_state;        /* [n] pointers to [H_v][d_k][d_v] states, in/out  */
   const void *z;               /* [n][H_v*d_v] or NULL                          */
   const void *norm_w;          /* [d_v] (with z)                                */
   void *out;                   /* [n][H_v*d_v]                                  */
@@ -208,6 +255,7 @@ typedef struct gdn_decode_args {
   float l2_eps;
   float norm_eps;
   float reserved_f;            /* must be 0                                     */
+  gdn_options opt;
 } gdn_decode_args;
 
 gdn_status gdn_decode_batched(const gdn_decode_args *args, void *stream);
@@ -242,7 +290,7 @@ typedef struct gdn_verify_args {
   void *const *conv_state;     /* [n] pointers, read only                       */
   const float *a;              /* [total_rows][H_v]                             */
   const float *b;              /* [total_rows][H_v]                             */
-  float *const *wy_tables;     /* [16][128] state pointers (this layer's slice)  */
+  void *const *wy_tables;      /* [16][128] state pointers (this layer's slice)  */
   const void *z;               /* [total_rows][H_v*d_v] or NULL                 */
   const void *norm_w;          /* [d_v] (with z)                                */
   void *out;                   /* [total_rows][H_v*d_v]                         */
@@ -250,6 +298,8 @@ typedef struct gdn_verify_args {
   float l2_eps;
   float norm_eps;
   float reserved_f;            /* must be 0                                     */
+  gdn_options opt;             /* with binary16 states every stored state, and the
+                                  state carried to the next row, is rounded     */
 } gdn_verify_args;
 
 gdn_status gdn_verify_multi(const gdn_verify_args *args, void *stream);
@@ -270,17 +320,140 @@ typedef struct gdn_commit_args {
   int32_t reserved;            /* must be 0                                     */
   const int32_t *cu_ks;        /* [n+1]                                         */
   const int32_t *n_accepted;   /* [n]                                           */
-  float *const *wy_tables;     /* [16][128]                                     */
+  void *const *wy_tables;      /* [16][128]                                     */
   const void *x;               /* [sum k][conv_dim] rows given to the verify    */
   void *const *conv_state;     /* [n] pointers, in/out                          */
+  gdn_options opt;             /* state_dtype only                              */
 } gdn_commit_args;
 
 gdn_status gdn_verify_commit(const gdn_commit_args *args, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * gdn_verify_woa -- write-on-accept verify: the rows, outputs and limits of
+ *   gdn_verify_multi, but no state is written.  Each sequence's state is read from
+ *   *h_state[i]; for every packed row r the call stores in stash row r what the
+ *   rank-1 update S_r = a_r S_{r-1} + u_r k_r^T needs:
+ *       stash[r * row_floats + g * d_k + j]                k_hat of key head g
+ *       stash[r * row_floats + H_k*d_k + h * d_v + j]      u of value head h
+ *       stash[r * row_floats + H_k*d_k + H_v*d_v + h]      a_r of value head h
+ *   with row_floats = H_k*d_k + H_v*d_v + H_v rounded up to a multiple of 4, and
+ *   u = b (v - a S k) computed from the state the row starts from.
+ *   gdn_fold_accepted then applies the accepted rows to the state.  The verify
+ *   moves one state read per sequence instead of k_i state writes.
+ *   Defined by: the write-on-accept handles gdn_wy4_woa_k, gdn_wy4_fold_k and the
+ *   woa_stash binding (layer_struct.rs), gdn_woa_stash_seq_floats, gdn_woa_bind
+ *   and gdn_fold_accepted (trait_layer.rs).  The pages name the stash, not its
+ *   contents; the (k_hat, u, a) rows are the plainest contents that let the fold
+ *   reproduce the recorded states exactly.
+ * ------------------------------------------------------------------------- */
+typedef struct gdn_woa_args {
+  uint32_t struct_size;        /* sizeof(gdn_woa_args)                          */
+  int32_t act_dtype;
+  int32_t out_dtype;
+  gdn_dims dims;
+  int32_t num_seqs;            /* n in 0..128                                   */
+  int32_t max_k;               /* host: upper bound of every k_i, 2..16         */
+  int32_t total_rows;          /* host: sum of k_i = cu_ks[n]                   */
+  int32_t reserved;            /* must be 0                                     */
+  const int32_t *cu_ks;        /* [n+1] row offsets                             */
+  const void *x;               /* [total_rows][conv_dim]                        */
+  const void *conv_w;          /* [conv_dim][K]                                 */
+  void *const *conv_state;     /* [n] pointers, read only                       */
+  const float *a;              /* [total_rows][H_v]                             */
+  const float *b;              /* [total_rows][H_v]                             */
+  void *const *h_state;        /* [n] pointers to [H_v][d_k][d_v], read only     */
+  const void *z;               /* [total_rows][H_v*d_v] or NULL                 */
+  const void *norm_w;          /* [d_v] (with z)                                */
+  void *out;                   /* [total_rows][H_v*d_v]                         */
+  float *stash;                /* [total_rows][row_floats] fp32, out             */
+  size_t stash_bytes;          /* bytes available at stash                      */
+  float scale;
+  float l2_eps;
+  float norm_eps;
+  float reserved_f;            /* must be 0                                     */
+  gdn_options opt;
+} gdn_woa_args;
+
+/* Bytes of stash gdn_verify_woa needs for these arguments (pointers are not
+ * read): total_rows * row_floats * 4.  Writes *bytes; returns the validation
+ * status. */
+gdn_status gdn_woa_stash_bytes(const gdn_woa_args *args, size_t *bytes /* host */);
+
+gdn_status gdn_verify_woa(const gdn_woa_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * gdn_fold_accepted -- apply the accepted rows of a write-on-accept verify.
+ *   For sequence i with n_i accepted rows (1 <= n_i <= k_i, the caller's
+ *   contract, as for gdn_verify_commit): for r = cu_ks[i] .. cu_ks[i] + n_i - 1 in
+ *   order, every value head's state becomes a_r S + u_r k_r^T (rounded after every
+ *   row when the state is binary16), reading stash row r; the state is read and
+ *   written once.  The conv state becomes the last K-1 rows of
+ *   [old conv state ; rows 0..n_i-1].  The result equals the state
+ *   gdn_verify_multi records after row n_i - 1.
+ *   Defined by: gdn_fold_accepted (trait_layer.rs), gdn_wy4_fold_k (layer_struct.rs).
+ * ------------------------------------------------------------------------- */
+typedef struct gdn_fold_args {
+  uint32_t struct_size;        /* sizeof(gdn_fold_args)                         */
+  int32_t act_dtype;           /* dtype of x and the conv states                */
+  gdn_dims dims;
+  int32_t num_seqs;            /* n in 0..128                                   */
+  int32_t total_rows;          /* host: cu_ks[n]                                */
+  const int32_t *cu_ks;        /* [n+1], as given to gdn_verify_woa             */
+  const int32_t *n_accepted;   /* [n]                                           */
+  void *const *h_state;        /* [n] pointers, in/out                          */
+  const float *stash;          /* written by gdn_verify_woa                     */
+  size_t stash_bytes;
+  const void *x;               /* [total_rows][conv_dim] rows given to the verify */
+  void *const *conv_state;     /* [n] pointers, in/out                          */
+  gdn_options opt;             /* state_dtype only                              */
+} gdn_fold_args;
+
+gdn_status gdn_fold_accepted(const gdn_fold_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * gdn_decode_tokens -- k_i consecutive tokens for each of n sequences in one
+ *   launch, equal to k_i gdn_decode_batched steps in a row: conv rows use the conv
+ *   state and the earlier rows, outputs for every token, and each sequence's
+ *   state (*h_state[i]) and conv state advance over all k_i tokens, the state
+ *   being read and written once.  Rows are packed sequence-major.
+ *   Limits: n <= 128, 1 <= k_i <= max_tokens <= GDN_DECODE_MAX_TOKENS.
+ *   Defined by: decode_batched, the k-consecutive-token decode of one sequence
+ *   (transformer_layer.rs page), batched over sequences as decode_multi_seq is;
+ *   gated_delta_rule_wy17 for K = 17 (layer_struct.rs).
+ * ------------------------------------------------------------------------- */
+typedef struct gdn_tokens_args {
+  uint32_t struct_size;        /* sizeof(gdn_tokens_args)                       */
+  int32_t act_dtype;
+  int32_t out_dtype;
+  gdn_dims dims;
+  int32_t num_seqs;            /* n in 0..128                                   */
+  int32_t max_tokens;          /* host: upper bound of every k_i, 1..17         */
+  int32_t total_rows;          /* host: cu_tokens[n]                            */
+  int32_t reserved;            /* must be 0                                     */
+  const int32_t *cu_tokens;    /* [n+1] row offsets                             */
+  const void *x;               /* [total_rows][conv_dim]                        */
+  const void *conv_w;          /* [conv_dim][K]                                 */
+  void *const *conv_state;     /* [n] pointers, in/out                          */
+  const float *a;              /* [total_rows][H_v]                             */
+  const float *b;              /* [total_rows][H_v]                             */
+  void *const *h_state;        /* [n] pointers, in/out                          */
+  const void *z;               /* [total_rows][H_v*d_v] or NULL                 */
+  const void *norm_w;          /* [d_v] (with z)                                */
+  void *out;                   /* [total_rows][H_v*d_v]                         */
+  float scale;
+  float l2_eps;
+  float norm_eps;
+  float reserved_f;            /* must be 0                                     */
+  gdn_options opt;
+} gdn_tokens_args;
+
+gdn_status gdn_decode_tokens(const gdn_tokens_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------
  * gdn_gated_rmsnorm -- out = o / sqrt(mean_j o_j^2 + eps) * w * SiLU(z), per
  *   (token, value head) over d_v.
- *   Defined by: gated_rms_norm_k, gated_rms_norm_prefill_k (layer_struct.rs).
+ *   Defined by: gated_rms_norm_k, gated_rms_norm_prefill_k (layer_struct.rs);
+ *   sigmoid(z) in place of SiLU(z) with opt.norm_gate = GDN_NORM_GATE_SIGMOID.
  * ------------------------------------------------------------------------- */
 typedef struct gdn_norm_args {
   uint32_t struct_size;        /* sizeof(gdn_norm_args)                         */
@@ -295,6 +468,7 @@ typedef struct gdn_norm_args {
   void *out;                   /* [T][H_v*d_v]; may alias o                     */
   float eps;
   float reserved_f;            /* must be 0                                     */
+  gdn_options opt;             /* norm_gate only                                */
 } gdn_norm_args;
 
 gdn_status gdn_gated_rmsnorm(const gdn_norm_args *args, void *stream);

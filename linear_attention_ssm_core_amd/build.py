@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["api.cpp", "recurrent.hip", "conv_norm.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "recurrent_decode.hip", "recurrent_tokens.hip", "recurrent_verify.hip", "recurrent_woa.hip",
+           "commit_fold.hip", "conv_norm.hip", "prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall", "-Wextra",

@@ -41,6 +41,34 @@ gdn_status check_dims(const gdn_dims &d, int32_t act_dtype, int32_t out_dtype, G
   return GDN_OK;
 }
 
+// Options an entry point takes: every option it does not take must be zero.
+struct Opts {
+  int state_f16, gates_raw, norm_sigmoid;
+};
+gdn_status check_opts(const gdn_options &o, bool takes_state, bool takes_gates, bool takes_norm, Opts *out) {
+  if (o.reserved != 0) return GDN_ERR_INVALID_ARG;
+  if (o.state_dtype != GDN_DTYPE_F32 && !(takes_state && o.state_dtype == GDN_DTYPE_F16))
+    return GDN_ERR_INVALID_ARG;
+  if (o.gate_mode != GDN_GATES_DIRECT && !(takes_gates && o.gate_mode == GDN_GATES_RAW))
+    return GDN_ERR_INVALID_ARG;
+  if (o.norm_gate != GDN_NORM_GATE_SILU && !(takes_norm && o.norm_gate == GDN_NORM_GATE_SIGMOID))
+    return GDN_ERR_INVALID_ARG;
+  out->state_f16 = o.state_dtype == GDN_DTYPE_F16;
+  out->gates_raw = o.gate_mode == GDN_GATES_RAW;
+  out->norm_sigmoid = o.norm_gate == GDN_NORM_GATE_SIGMOID;
+  return GDN_OK;
+}
+
+void set_opts(gdn::RecurrentLaunch *p, const Opts &o) {
+  p->state_f16 = o.state_f16;
+  p->gates_raw = o.gates_raw;
+  p->norm_sigmoid = o.norm_sigmoid;
+}
+
+// Floats per write-on-accept stash row: k_hat of every key head, u of every value
+// head, a of every value head, rounded up to whole 16-byte vectors.
+int stash_row_floats(const Geometry &g) { return (g.Hk * g.D + g.Hv * g.D + g.Hv + 3) & ~3; }
+
 bool finite(float v) { return std::isfinite(v); }
 bool eps_ok(float v) { return std::isfinite(v) && v >= 0.0f; }
 
@@ -52,6 +80,7 @@ struct PrefillPlan {
   Geometry geo;
   bool fused_front, epilogue;
   size_t y_bytes, o_bytes, core_bytes, total;
+  Opts opts;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -67,6 +96,8 @@ gdn_status plan_prefill(const gdn_prefill_args *a, PrefillPlan *plan) {
   if (a->total_tokens > ((int64_t)1 << 31) - 1) return GDN_ERR_INVALID_ARG;
   if (a->total_tokens > 0 && a->num_seqs == 0) return GDN_ERR_INVALID_ARG;
   if (!finite(a->scale) || !eps_ok(a->l2_eps) || !eps_ok(a->norm_eps)) return GDN_ERR_INVALID_ARG;
+  s = check_opts(a->opt, true, true, true, &plan->opts);
+  if (s != GDN_OK) return s;
   plan->fused_front = a->x != nullptr;
   plan->epilogue = a->z != nullptr;
   const int64_t T = a->total_tokens;
@@ -133,8 +164,12 @@ gdn_status gdn_decode_batched(const gdn_decode_args *a, void *stream) {
        a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
   if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  Opts o;
+  s = check_opts(a->opt, true, true, true, &o);
+  if (s != GDN_OK) return s;
+  set_opts(&p, o);
   p.n = a->num_seqs;
-  p.verify = 0;
+  p.mode = gdn::kModeDecode;
   p.cu = nullptr;
   p.x = a->x;
   p.conv_w = a->conv_w;
@@ -166,8 +201,12 @@ gdn_status gdn_verify_multi(const gdn_verify_args *a, void *stream) {
        a->a == nullptr || a->b == nullptr || a->wy_tables == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
   if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  Opts o;
+  s = check_opts(a->opt, true, true, true, &o);
+  if (s != GDN_OK) return s;
+  set_opts(&p, o);
   p.n = a->num_seqs;
-  p.verify = 1;
+  p.mode = gdn::kModeVerify;
   p.cu = a->cu_ks;
   p.x = a->x;
   p.conv_w = a->conv_w;
@@ -194,6 +233,10 @@ gdn_status gdn_verify_commit(const gdn_commit_args *a, void *stream) {
   if (a->num_seqs > 0 && (a->cu_ks == nullptr || a->n_accepted == nullptr || a->wy_tables == nullptr ||
                           a->x == nullptr || a->conv_state == nullptr))
     return GDN_ERR_INVALID_ARG;
+  Opts o;
+  s = check_opts(a->opt, true, false, false, &o);
+  if (s != GDN_OK) return s;
+  p.state_f16 = o.state_f16;
   p.n = a->num_seqs;
   p.cu = a->cu_ks;
   p.n_accepted = a->n_accepted;
@@ -215,7 +258,11 @@ gdn_status gdn_gated_rmsnorm(const gdn_norm_args *a, void *stream) {
   if (a->total_tokens * d.num_v_heads > ((int64_t)1 << 33)) return GDN_ERR_INVALID_ARG;
   if (a->total_tokens > 0 && (a->o == nullptr || a->z == nullptr || a->norm_w == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
+  Opts o;
+  gdn_status s = check_opts(a->opt, false, false, true, &o);
+  if (s != GDN_OK) return s;
   gdn::NormLaunch p{};
+  p.norm_sigmoid = o.norm_sigmoid;
   p.Hv = d.num_v_heads;
   p.D = d.head_dim_v;
   p.T = a->total_tokens;
@@ -289,7 +336,9 @@ gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
   p.y_bf16 = y_bf16;
   p.a = a->a;
   p.b = a->b;
+  p.gates_raw = plan.opts.gates_raw;
   p.h_state = a->h_state;
+  p.state_f16 = plan.opts.state_f16;
   p.o = plan.epilogue ? static_cast<void *>(ws + plan.y_bytes) : a->out;
   p.o_f32 = plan.epilogue ? 1 : 0;
   p.scale = a->scale;
@@ -304,6 +353,7 @@ gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
     nl.in_bf16 = 0;
     nl.act_bf16 = g.act_bf16;
     nl.out_bf16 = g.out_bf16;
+    nl.norm_sigmoid = plan.opts.norm_sigmoid;
     nl.o = p.o;
     nl.z = a->z;
     nl.norm_w = a->norm_w;
@@ -313,6 +363,122 @@ gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
   return GDN_OK;
+}
+
+gdn_status gdn_woa_stash_bytes(const gdn_woa_args *a, size_t *bytes) {
+  if (bytes == nullptr) return GDN_ERR_INVALID_ARG;
+  *bytes = 0;
+  if (a == nullptr || a->struct_size != sizeof(gdn_woa_args)) return GDN_ERR_INVALID_ARG;
+  Geometry geo;
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &geo);
+  if (s != GDN_OK) return s;
+  if (a->total_rows < 0) return GDN_ERR_INVALID_ARG;
+  *bytes = (size_t)a->total_rows * stash_row_floats(geo) * sizeof(float);
+  return GDN_OK;
+}
+
+gdn_status gdn_verify_woa(const gdn_woa_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_woa_args)) return GDN_ERR_INVALID_ARG;
+  gdn::RecurrentLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->num_seqs > GDN_VERIFY_WY_TABLE_SEQS) return GDN_ERR_INVALID_ARG;
+  if (a->max_k < GDN_VERIFY_MIN_K || a->max_k > GDN_VERIFY_MAX_K) return GDN_ERR_INVALID_ARG;
+  if (a->total_rows < 0 || a->total_rows > a->num_seqs * a->max_k) return GDN_ERR_INVALID_ARG;
+  if (a->reserved != 0 || a->reserved_f != 0.0f) return GDN_ERR_INVALID_ARG;
+  if (!finite(a->scale) || !eps_ok(a->l2_eps) || !eps_ok(a->norm_eps)) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 &&
+      (a->cu_ks == nullptr || a->x == nullptr || a->conv_w == nullptr || a->conv_state == nullptr ||
+       a->a == nullptr || a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  Opts o;
+  s = check_opts(a->opt, true, true, true, &o);
+  if (s != GDN_OK) return s;
+  const size_t need = (size_t)a->total_rows * stash_row_floats(p.geo) * sizeof(float);
+  if (a->num_seqs > 0 && (a->stash == nullptr || a->stash_bytes < need)) return GDN_ERR_WORKSPACE;
+  set_opts(&p, o);
+  p.n = a->num_seqs;
+  p.mode = gdn::kModeWoa;
+  p.cu = a->cu_ks;
+  p.x = a->x;
+  p.conv_w = a->conv_w;
+  p.conv_state = a->conv_state;
+  p.a = a->a;
+  p.b = a->b;
+  p.states = a->h_state;
+  p.z = a->z;
+  p.norm_w = a->norm_w;
+  p.out = a->out;
+  p.stash = a->stash;
+  p.stash_row = stash_row_floats(p.geo);
+  p.scale = a->scale;
+  p.l2_eps = a->l2_eps;
+  p.norm_eps = a->norm_eps;
+  return hip_status(gdn::launch_recurrent(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_fold_accepted(const gdn_fold_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_fold_args)) return GDN_ERR_INVALID_ARG;
+  gdn::FoldLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, GDN_DTYPE_F32, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->num_seqs > GDN_VERIFY_WY_TABLE_SEQS || a->total_rows < 0) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 && (a->cu_ks == nullptr || a->n_accepted == nullptr || a->h_state == nullptr ||
+                          a->x == nullptr || a->conv_state == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  Opts o;
+  s = check_opts(a->opt, true, false, false, &o);
+  if (s != GDN_OK) return s;
+  const size_t need = (size_t)a->total_rows * stash_row_floats(p.geo) * sizeof(float);
+  if (a->num_seqs > 0 && (a->stash == nullptr || a->stash_bytes < need)) return GDN_ERR_WORKSPACE;
+  p.n = a->num_seqs;
+  p.state_f16 = o.state_f16;
+  p.cu = a->cu_ks;
+  p.n_accepted = a->n_accepted;
+  p.states = a->h_state;
+  p.stash = a->stash;
+  p.stash_row = stash_row_floats(p.geo);
+  p.x = a->x;
+  p.conv_state = a->conv_state;
+  return hip_status(gdn::launch_fold(p, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_decode_tokens(const gdn_tokens_args *a, void *stream) {
+  if (a == nullptr || a->struct_size != sizeof(gdn_tokens_args)) return GDN_ERR_INVALID_ARG;
+  gdn::RecurrentLaunch p{};
+  gdn_status s = check_dims(a->dims, a->act_dtype, a->out_dtype, &p.geo);
+  if (s != GDN_OK) return s;
+  if (a->num_seqs < 0 || a->num_seqs > GDN_VERIFY_WY_TABLE_SEQS) return GDN_ERR_INVALID_ARG;
+  if (a->max_tokens < 1 || a->max_tokens > GDN_DECODE_MAX_TOKENS) return GDN_ERR_INVALID_ARG;
+  if (a->total_rows < 0 || a->total_rows > a->num_seqs * a->max_tokens) return GDN_ERR_INVALID_ARG;
+  if (a->reserved != 0 || a->reserved_f != 0.0f) return GDN_ERR_INVALID_ARG;
+  if (!finite(a->scale) || !eps_ok(a->l2_eps) || !eps_ok(a->norm_eps)) return GDN_ERR_INVALID_ARG;
+  if (a->num_seqs > 0 &&
+      (a->cu_tokens == nullptr || a->x == nullptr || a->conv_w == nullptr || a->conv_state == nullptr ||
+       a->a == nullptr || a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
+    return GDN_ERR_INVALID_ARG;
+  if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  Opts o;
+  s = check_opts(a->opt, true, true, true, &o);
+  if (s != GDN_OK) return s;
+  set_opts(&p, o);
+  p.n = a->num_seqs;
+  p.mode = gdn::kModeTokens;
+  p.cu = a->cu_tokens;
+  p.x = a->x;
+  p.conv_w = a->conv_w;
+  p.conv_state = a->conv_state;
+  p.a = a->a;
+  p.b = a->b;
+  p.states = a->h_state;
+  p.z = a->z;
+  p.norm_w = a->norm_w;
+  p.out = a->out;
+  p.scale = a->scale;
+  p.l2_eps = a->l2_eps;
+  p.norm_eps = a->norm_eps;
+  return hip_status(gdn::launch_recurrent(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,153 @@
+// Commit of a verify's accepted prefix, and the fold of a write-on-accept
+// verify's accepted rows (gdn_fold_accepted on the
+// metrale_model_layers/layers/qwen3_ssm/trait_layer.rs page; gdn_wy4_fold_k on the
+// layer_struct.rs page).  Both also advance the conv state over the accepted rows.
+#include "recurrent_kernel.h"
+
+namespace gdn {
+namespace {
+
+// blockIdx.y < kCommitSplit: one eighth of the state copy, 8 loads in flight per
+// thread; otherwise conv-state channels.
+constexpr int kCommitSplit = 8;
+constexpr int kMaxFoldRows = 16;
+
+// The conv state of sequence i becomes the last K-1 rows of
+// [old conv state ; its first na rows]; channel c = cblk * 256 + threadIdx.x.
+template <typename TE>
+__device__ __forceinline__ void advance_ring(const Geometry &geo, void *const *conv_state, const void *xv,
+                                             const int32_t *cu, int i, int na, int cblk) {
+  const int C = geo.conv_dim, R = geo.K - 1;
+  const int c = cblk * 256 + threadIdx.x;
+  if (c >= C) return;
+  TE *ring = static_cast<TE *>(conv_state[i]);
+  const TE *x = static_cast<const TE *>(xv) + (size_t)cu[i] * C;
+  TE vals[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {  // position na + r of [old conv state ; accepted rows]
+    const int idx = na + min(r, R - 1);
+    const TE vr = ring[(size_t)min(idx, R - 1) * C + c], vx = x[(size_t)max(idx - R, 0) * C + c];
+    vals[r] = (idx < R) ? vr : vx;
+  }
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    if (r < R) ring[(size_t)r * C + c] = vals[r];
+}
+
+// Commit: copy the state after the last accepted row into table 0.
+template <typename TE>
+__global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4) {
+  const int i = blockIdx.x;
+  const int k = p.cu[i + 1] - p.cu[i];
+  const int na = p.n_accepted[i];
+  if (na < 1 || na > k) return;  // outside the caller's contract: sequence untouched
+  if ((int)blockIdx.y < kCommitSplit) {
+    if (na == k) return;  // table 0 already holds the last state
+    // (native 4-float vectors: the struct-based float4 array ends up in scratch)
+    const gptr<const floatx4> src = to_global(static_cast<const floatx4 *>(p.tables[na * kTableSeqs + i]));
+    const gptr<floatx4> dst = to_global(static_cast<floatx4 *>(p.tables[i]));
+    const int64_t per = (n4 + kCommitSplit - 1) / kCommitSplit;
+    const int64_t beg = (int64_t)blockIdx.y * per, end = min(n4, beg + per);
+    // whole tiles of 256 x 8 vectors without conditions, then the tail
+    int64_t i0 = beg;
+    for (; i0 + 256 * 8 <= end; i0 += 256 * 8) {
+      floatx4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[i0 + threadIdx.x + u * 256];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dst[i0 + threadIdx.x + u * 256] = v[u];
+    }
+    for (int64_t idx = i0 + threadIdx.x; idx < end; idx += 256) dst[idx] = src[idx];
+  } else {
+    advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.y - kCommitSplit);
+  }
+}
+
+// Fold: blockIdx.y < H_v is one value head's state, read once, advanced over the
+// accepted rows from the stash in order (the verify's rank-1 update, bit for bit),
+// and written once; the other blocks advance the conv state.  Thread t holds
+// column quad t % (D/4) of rows rr * (1024/D) + t / (D/4), as in the verify.
+template <int D, typename TE, typename TS>
+__global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
+  constexpr int CQ = D / 4, RG = kSlot / CQ, RPT = D / RG;
+  __shared__ float s_k[kMaxFoldRows][D], s_u[kMaxFoldRows][D], s_a[kMaxFoldRows];
+  const int i = blockIdx.x;
+  const int r0 = p.cu[i];
+  const int k = p.cu[i + 1] - r0;
+  const int na = p.n_accepted[i];
+  if (na < 1 || na > k || na > kMaxFoldRows) return;  // outside the caller's contract
+  const int Hv = p.geo.Hv, Hk = p.geo.Hk;
+  if ((int)blockIdx.y >= Hv) {
+    advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.y - Hv);
+    return;
+  }
+  const int h = blockIdx.y, g = h / (Hv / Hk);
+  const int t = threadIdx.x, cq = t % CQ, rg = t / CQ;
+  const gptr<TS> S = to_global(static_cast<TS *>(p.states[i])) + (size_t)h * D * D;
+  typename StateIO<TS>::raw st_raw[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S + (size_t)(rr * RG + rg) * D + 4 * cq);
+  const gptr<const float> stash = to_global(p.stash) + (size_t)r0 * p.stash_row;
+  for (int e = t; e < na * D; e += kSlot) {
+    const int r = e / D, j = e - r * D;
+    s_k[r][j] = stash[(size_t)r * p.stash_row + g * D + j];
+    s_u[r][j] = stash[(size_t)r * p.stash_row + Hk * D + h * D + j];
+  }
+  if (t < na) s_a[t] = stash[(size_t)t * p.stash_row + Hk * D + Hv * D + h];
+  __syncthreads();
+  floatx4 st_reg[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) st_reg[rr] = StateIO<TS>::widen(st_raw[rr]);
+  for (int r = 0; r < na; ++r) {
+    const float av = s_a[r];
+    const floatx4 u = *reinterpret_cast<const floatx4 *>(&s_u[r][4 * cq]);
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr)
+      st_reg[rr] = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, s_k[r][rr * RG + rg], u));
+  }
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) StateIO<TS>::store(S + (size_t)(rr * RG + rg) * D + 4 * cq, st_reg[rr]);
+}
+
+template <int D, typename TE>
+hipError_t launch_fold_ts(const FoldLaunch &p, hipStream_t stream) {
+  const int nblk_ring = (p.geo.conv_dim + 255) / 256;
+  const dim3 grid(p.n, p.geo.Hv + nblk_ring), block(kSlot);
+  if (p.state_f16)
+    hipLaunchKernelGGL((fold_kernel<D, TE, _Float16>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((fold_kernel<D, TE, float>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fold_d(const FoldLaunch &p, hipStream_t stream) {
+  return p.geo.act_bf16 ? launch_fold_ts<D, uint16_t>(p, stream) : launch_fold_ts<D, float>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_commit(const CommitLaunch &p, hipStream_t stream) {
+  if (p.n == 0) return hipSuccess;
+  // 16-byte vectors per sequence state: 4 fp32 or 8 binary16 elements each
+  const int64_t n4 = (int64_t)p.geo.Hv * p.geo.D * p.geo.D / (p.state_f16 ? 8 : 4);
+  const int nblk_ring = (p.geo.conv_dim + 255) / 256;
+  const dim3 grid(p.n, kCommitSplit + nblk_ring), block(256);
+  if (p.geo.act_bf16)
+    hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, n4);
+  else
+    hipLaunchKernelGGL((commit_kernel<float>), grid, block, 0, stream, p, n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const FoldLaunch &p, hipStream_t stream) {
+  if (p.n == 0) return hipSuccess;
+  switch (p.geo.D) {
+    case 32: return launch_fold_d<32>(p, stream);
+    case 64: return launch_fold_d<64>(p, stream);
+    case 128: return launch_fold_d<128>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -4,7 +4,8 @@
 //    metrale_model_layers/layers/qwen3_ssm/layer_struct.rs page), and the
 //    advance of each sequence's conv state;
 //  * Z-gated RMSNorm per (token, value head) (gated_rms_norm_k,
-//    gated_rms_norm_prefill_k, same page).
+//    gated_rms_norm_prefill_k, same page), gate SiLU(z) or, for a model of the
+//    gdn_norm_sigmoid kind, sigmoid(z).
 //
 // Both are streaming, HBM-bound kernels with 16-byte accesses.  The conv state is
 // advanced by a second small kernel, ordered after the first on the stream,
@@ -253,7 +254,8 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormLaunch p) {
   const float inv = rsqrt_hw(ss / D + p.eps);
   float res[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) res[e] = ov[e] * inv * wv[e] * silu(zv[e]);
+  for (int e = 0; e < 8; ++e)
+    res[e] = ov[e] * inv * wv[e] * (p.norm_sigmoid ? __builtin_amdgcn_rcpf(1.0f + __expf(-zv[e])) : silu(zv[e]));
   if (active) store8(out + (size_t)r * D + c0, res);
 }
 

@@ -16,18 +16,30 @@ struct Geometry {
   int out_bf16;         // output dtype is bf16 (else fp32)
 };
 
-// One-token decode (rows == sequences) and k-row verify share one kernel family.
+// The token-recurrent forms share one kernel family.
+enum RecurrentMode {
+  kModeDecode = 0,   // one token per sequence: state and conv state advance in place
+  kModeTokens = 1,   // up to 17 tokens per sequence, state written once at the end
+  kModeVerify = 2,   // k rows, the state after every row stored through the WY tables
+  kModeWoa = 3       // k rows, no state stored; (k_hat, u, a) of every row stashed
+};
+
 struct RecurrentLaunch {
   Geometry geo;
   int n;                        // sequences
-  int verify;                   // 0: decode, 1: verify
-  const int32_t *cu;            // verify row offsets [n+1] (device), unused for decode
+  int mode;                     // RecurrentMode
+  int state_f16;                // states are binary16 (else fp32)
+  int gates_raw;                // a, b hold g and beta
+  int norm_sigmoid;             // the norm gate is sigmoid(z) (else SiLU(z))
+  const int32_t *cu;            // row offsets [n+1] (device), unused for decode
   const void *x, *conv_w;
   void *const *conv_state;
   const float *a, *b;
-  float *const *states;         // decode: [n] state pointers; verify: [16][128] tables
+  void *const *states;          // decode/tokens/woa: [n] state pointers; verify: [16][128] tables
   const void *z, *norm_w;
   void *out;
+  float *stash;                 // woa: [rows][stash_row] floats
+  int stash_row;                // floats per stash row
   float scale, l2_eps, norm_eps;
 };
 hipError_t launch_recurrent(const RecurrentLaunch &p, hipStream_t stream);
@@ -35,12 +47,27 @@ hipError_t launch_recurrent(const RecurrentLaunch &p, hipStream_t stream);
 struct CommitLaunch {
   Geometry geo;
   int n;
+  int state_f16;
   const int32_t *cu, *n_accepted;
-  float *const *tables;
+  void *const *tables;
   const void *x;
   void *const *conv_state;
 };
 hipError_t launch_commit(const CommitLaunch &p, hipStream_t stream);
+
+// Fold of the accepted rows of a write-on-accept verify.
+struct FoldLaunch {
+  Geometry geo;
+  int n;
+  int state_f16;
+  const int32_t *cu, *n_accepted;
+  void *const *states;          // [n] state pointers
+  const float *stash;
+  int stash_row;
+  const void *x;
+  void *const *conv_state;
+};
+hipError_t launch_fold(const FoldLaunch &p, hipStream_t stream);
 
 struct ConvLaunch {
   Geometry geo;
@@ -59,6 +86,7 @@ struct NormLaunch {
   int Hv, D;
   int64_t T;
   int in_bf16, act_bf16, out_bf16;
+  int norm_sigmoid;             // gate sigmoid(z) (else SiLU(z))
   const void *o, *z, *norm_w;
   void *out;
   float eps;
@@ -73,7 +101,9 @@ struct PrefillLaunch {
   const void *y;                // [T][conv_dim] q_hat|k_hat|v
   int y_bf16;                   // dtype of y
   const float *a, *b;
-  float *const *h_state;
+  int gates_raw;                // a, b hold g and beta
+  void *const *h_state;
+  int state_f16;                // states are binary16 (else fp32)
   void *o;                      // [T][Hv*D] written by the chunk kernels
   int o_f32;                    // o is fp32 (else geo.out_bf16 decides)
   float scale;

@@ -257,8 +257,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   if (wave == 0) {
     const size_t gi = (size_t)(t0 + min(lane, L - 1)) * Hv + h;
     const float a_raw = p.a[gi], b_raw = p.b[gi];
-    float la = (lane < L) ? fmaxf(logf(a_raw), -30.0f) : 0.0f;
-    const float bb = (lane < L) ? b_raw : 0.0f;
+    // ln a, clamped at -30; from raw gate inputs ln a = -softplus(g) and b = sigmoid(beta)
+    const float ln_a = p.gates_raw ? -(fmaxf(a_raw, 0.0f) + log1pf(expf(-fabsf(a_raw)))) : logf(a_raw);
+    float la = (lane < L) ? fmaxf(ln_a, -30.0f) : 0.0f;
+    const float bb = (lane < L) ? (p.gates_raw ? 1.0f / (1.0f + expf(-b_raw)) : b_raw) : 0.0f;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const float v = __shfl_up(la, off);
@@ -575,7 +577,10 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   const TY *y = static_cast<const TY *>(p.y);
   TO *o = static_cast<TO *>(p.o);
   const size_t ostride = (size_t)Hv * D;
-  gptr<float> hs = to_global(p.h_state[seq]) + (size_t)h * D * D + kCols * cb;
+  // the sequence's state: fp32, or binary16 widened here and narrowed at the end
+  const size_t hoff = (size_t)h * D * D + kCols * cb;
+  gptr<float> hs = to_global(static_cast<float *>(p.h_state[seq])) + hoff;
+  gptr<_Float16> hs16 = to_global(static_cast<_Float16 *>(p.h_state[seq])) + hoff;
   auto unit_of = [&](int c) { return units + ((size_t)(c_first + c) * Hv + h) * unit_bytes(D); };
   auto gam_of = [&](int c) {
     return reinterpret_cast<const float *>(reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC + 2 * kC * kC);
@@ -762,7 +767,10 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hacc[t][ct][r] = hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct];
+        for (int r = 0; r < 4; ++r) {
+          const size_t e = (size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct;
+          hacc[t][ct][r] = p.state_f16 ? (float)hs16[e] : hs[e];
+        }
         const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
         store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
                      &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
@@ -805,7 +813,13 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hs[(size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct] = hacc[t][ct][r];
+        for (int r = 0; r < 4; ++r) {
+          const size_t e = (size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct;
+          if (p.state_f16)
+            hs16[e] = (_Float16)hacc[t][ct][r];
+          else
+            hs[e] = hacc[t][ct][r];
+        }
   } else {
     // waves without state rows (d_k < 128): keep the barrier count
     __syncthreads();

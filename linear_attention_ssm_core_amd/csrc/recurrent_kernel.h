@@ -1,35 +1,85 @@
-// One-token batched decode, k-row verify with every intermediate state written
-// through the WY pointer tables, and the commit of the accepted prefix.
+// The token-recurrent kernel family: one-token batched decode, the decode of up
+// to 17 consecutive tokens per sequence, the k-row verify that stores every
+// intermediate state through the WY pointer tables, and the write-on-accept
+// verify that stashes each row's rank-1 update instead.
 //
 // Decode (decode_multi_seq on the metrale_model_layers/layer/transformer_layer.rs
 // page; the strided one-launch kernels conv1d_l2norm_f32_strided_k,
 // gdn_f32_strided_norm_k and gated_rms_norm_f32_strided_k on the
-// metrale_model_layers/layers/qwen3_ssm/layer_struct.rs page) and verify
-// (decode_verify_multi and the VERIFY_WY_* table constants, transformer_layer.rs;
-// gdn_wyn_table_k, gdn_f32_strided_norm_snap_k, layer_struct.rs) are one kernel:
-// verify runs k rows from the state in table 0 and stores the state after each
-// row, decode is one row that also advances the conv state.
+// metrale_model_layers/layers/qwen3_ssm/layer_struct.rs page), the k-token decode
+// (decode_batched, transformer_layer.rs; gated_delta_rule_wy17, layer_struct.rs),
+// verify (decode_verify_multi and the VERIFY_WY_* table constants,
+// transformer_layer.rs; gdn_wyn_table_k, gdn_f32_strided_norm_snap_k,
+// layer_struct.rs) and the write-on-accept verify (gdn_wy4_woa_k, layer_struct.rs)
+// are one kernel template: the mode decides which states are stored and whether
+// the conv state advances.
 //
 // Design (MI355X): the path is HBM-bound -- each value head's 128x128 fp32 state
-// (64 KiB) is read once and written once (decode) or k times (verify).  One
-// workgroup owns one (sequence, key head) pair: the conv + L2 prologue of the
-// shared q/k channels runs once and feeds the H_v/H_k value heads of the group
-// through LDS, and because one workgroup owns all channels of the group the
-// in-place conv-state update has no cross-workgroup race.  256 threads own one
-// value head: thread t holds column quad (t % 32) of rows {rr * 8 + t / 32}, so
-// every wave-wide 16-byte load or store covers whole contiguous 512-byte state
-// rows, and the state stays in registers across the k verify rows.  S k and S q
-// are reduced over row groups with wave shuffles and one LDS exchange per row.
-// All arithmetic is fp32 (the recurrence per token is
+// (64 KiB; 32 KiB as binary16) is read once and written once (decode, k-token
+// decode), k times (verify) or not at all (write-on-accept).  One workgroup owns
+// one (sequence, key head) pair: the conv + L2 prologue of the shared q/k channels
+// runs once and feeds the H_v/H_k value heads of the group through LDS, and
+// because one workgroup owns all channels of the group the in-place conv-state
+// update has no cross-workgroup race.  256 threads own one value head: thread t
+// holds column quad (t % 32) of rows {rr * 8 + t / 32}, so every wave-wide load or
+// store covers whole contiguous state rows, and the state stays in registers
+// across the rows of a sequence.  S k and S q are reduced over row groups with
+// wave shuffles and one LDS exchange per row.  All arithmetic is fp32 (the
+// recurrence per token is
 //   kv = S k;  u = b (v - a kv);  S <- a S + u k^T;  o = scale (a S q + (k.q) u),
-// the last being S_new q expanded).
+// the last being S_new q expanded); a binary16 state is rounded when stored and
+// the state carried to the next row is the stored value.
+#pragma once
+
 #include "common.h"
 #include "internal.h"
 
 namespace gdn {
-namespace {
 
 constexpr int kSlot = 256;          // threads per value head
+constexpr int kTableSeqs = 128;     // entries per WY pointer table
+// s_waitcnt immediate: vector-memory counter 0 (bits 3:0 and 15:14), expcnt and
+// lgkmcnt at their maxima (no wait)
+constexpr int kWaitVmem0 = (7 << 4) | (15 << 8);
+
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+// 4 consecutive state elements of either storage type: raw load, widening, and
+// the value a 4-vector takes once stored (binary16: rounded to nearest even).
+template <typename TS>
+struct StateIO;
+template <>
+struct StateIO<float> {
+  typedef floatx4 raw;
+  static __device__ __forceinline__ raw load(gptr<const float> p) { return *reinterpret_cast<gptr<const floatx4>>(p); }
+  static __device__ __forceinline__ floatx4 widen(raw r) { return r; }
+  static __device__ __forceinline__ floatx4 as_stored(floatx4 v) { return v; }
+  static __device__ __forceinline__ void store(gptr<float> p, floatx4 v) { *reinterpret_cast<gptr<floatx4>>(p) = v; }
+};
+template <>
+struct StateIO<_Float16> {
+  typedef halfx4 raw;
+  static __device__ __forceinline__ raw load(gptr<const _Float16> p) { return *reinterpret_cast<gptr<const halfx4>>(p); }
+  static __device__ __forceinline__ floatx4 widen(raw r) { return __builtin_convertvector(r, floatx4); }
+  static __device__ __forceinline__ floatx4 as_stored(floatx4 v) {
+    return __builtin_convertvector(__builtin_convertvector(v, halfx4), floatx4);
+  }
+  static __device__ __forceinline__ void store(gptr<_Float16> p, floatx4 v) {
+    *reinterpret_cast<gptr<halfx4>>(p) = __builtin_convertvector(v, halfx4);
+  }
+};
+
+// S <- a S + u k^T on one row of 4 columns: the same operation order in every
+// kernel that advances a state, so that a fold of stashed rows reproduces the
+// verify's recorded states bit for bit.
+__device__ __forceinline__ floatx4 rank1_update(floatx4 s, float a, float k, floatx4 u) {
+  floatx4 r;
+  r.x = __builtin_fmaf(k, u.x, a * s.x);
+  r.y = __builtin_fmaf(k, u.y, a * s.y);
+  r.z = __builtin_fmaf(k, u.z, a * s.z);
+  r.w = __builtin_fmaf(k, u.w, a * s.w);
+  return r;
+}
 
 __device__ __forceinline__ void store4(float *p, const float v[4]) {
   *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -43,25 +93,29 @@ __device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
   for (int e = 0; e < 4; ++e) w.b[e] = (bf16)v[e];
   *reinterpret_cast<uint2 *>(p) = w.u;
 }
-constexpr int kTableSeqs = 128;     // entries per WY pointer table
-// s_waitcnt immediate: vector-memory counter 0 (bits 3:0 and 15:14), expcnt and
-// lgkmcnt at their maxima (no wait)
-constexpr int kWaitVmem0 = (7 << 4) | (15 << 8);
 
-template <int D, int G, int MAXR, typename TA, typename TO>
+// Raw gate inputs: a = exp(-softplus(g)) = 1 / (1 + e^g), b = 1 / (1 + e^-beta).
+__device__ __forceinline__ float decay_from_raw(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(g)); }
+__device__ __forceinline__ float strength_from_raw(float beta) { return __builtin_amdgcn_rcpf(1.0f + __expf(-beta)); }
+
+template <int D, int G, int MAXR, int MODE, typename TA, typename TS>
 __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) {
   constexpr int CQ = D / 4;            // column quads of a head
   constexpr int RG = kSlot / CQ;       // row groups
   constexpr int RPT = D / RG;          // state rows held by a thread
   constexpr int NCH = (2 + G) * D;     // q, k, and G v heads
   constexpr int NT = kSlot * G;
+  constexpr bool kStoresEveryRow = MODE == kModeVerify;
+  constexpr bool kStoresLast = MODE == kModeDecode || MODE == kModeTokens;
+  constexpr bool kAdvancesRing = MODE == kModeDecode || MODE == kModeTokens;
   static_assert(RPT * RG == D, "head dim must split over the row groups");
+  static_assert((MODE == kModeDecode) == (MAXR == 1), "one-token decode is the MAXR = 1 instance");
 
   __shared__ float s_qkv[MAXR][NCH];
   __shared__ float s_a[MAXR][G], s_b[MAXR][G];
   __shared__ float s_qk[MAXR];
-  __shared__ float s_zw[MAXR][G * D];  // silu(z) * norm weight of the group's value channels
-  __shared__ float *s_dst[MAXR];       // where the state after each row is stored
+  __shared__ float s_zw[MAXR][G * D];  // gate(z) * norm weight of the group's value channels
+  __shared__ TS *s_dst[kStoresEveryRow ? MAXR : 1];  // verify: where the state after each row goes
   __shared__ float4 s_red[2][G][4][CQ][2];
 
   const int Hk = p.geo.Hk, Hv = p.geo.Hv, K = p.geo.K, C = p.geo.conv_dim;
@@ -70,13 +124,14 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   const int tid = threadIdx.x;
 
   int i, r0, nrows;
-  if (MAXR == 1) {
+  if (MODE == kModeDecode) {
     i = rank;
     r0 = i;
     nrows = 1;
   } else {
-    // verify: workgroups take sequences longest draft first, so the long ones
-    // do not trail at the end of the grid (ranks of the <= 128 lengths, ties by index)
+    // several rows per sequence: workgroups take sequences longest first, so the
+    // long ones do not trail at the end of the grid (ranks of the <= 128 lengths,
+    // ties by index)
     __shared__ int s_cu[kTableSeqs + 1];
     __shared__ int s_seq;
     for (int t = tid; t <= p.n; t += NT) s_cu[t] = p.cu[t];
@@ -130,8 +185,10 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   const float ga = p.a[(size_t)(r0 + min(gr, nrows - 1)) * Hv + g * G + gs];
   const float gb = p.b[(size_t)(r0 + min(gr, nrows - 1)) * Hv + g * G + gs];
   // destination of the state after row tid: table tid + 1, table 0 after the last
-  float *const dst_mid = p.states[(min(tid, max(nrows - 2, 0)) + (nrows > 1 ? 1 : 0)) * kTableSeqs + i];
-  float *const dst_last = p.states[i];
+  TS *dst_mid = nullptr;
+  if (kStoresEveryRow)
+    dst_mid = static_cast<TS *>(p.states[(min(tid, max(nrows - 2, 0)) + (nrows > 1 ? 1 : 0)) * kTableSeqs + i]);
+  TS *const dst_last = static_cast<TS *>(p.states[i]);
   const TA *zp = has_z ? static_cast<const TA *>(p.z) : x;
   const TA *nwp = has_z ? static_cast<const TA *>(p.norm_w) : x;
   const int zc = min(tid, G * D - 1);
@@ -145,11 +202,10 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   const int s = tid / kSlot, t = tid % kSlot;
   const int h = g * G + s;
   const int cq = t % CQ, rg = t / CQ;
-  const gptr<float> S_in = to_global(p.states[i]) + (size_t)h * D * D;  // table 0 / decode pointer
-  floatx4 st_reg[RPT];
+  const gptr<const TS> S_in = to_global(static_cast<const TS *>(p.states[i])) + (size_t)h * D * D;
+  typename StateIO<TS>::raw st_raw[RPT];
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr)
-    st_reg[rr] = *reinterpret_cast<const gptr<floatx4>>(S_in + (size_t)(rr * RG + rg) * D + 4 * cq);
+  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S_in + (size_t)(rr * RG + rg) * D + 4 * cq);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- prologue: conv + SiLU of the group's channels for every row ----------
@@ -172,22 +228,25 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
       win[1] = win[2];
       win[2] = xv;
     }
-    if (MAXR == 1) {  // decode advances the conv state by one row: new rows are t-2, t-1, t
+    if (kAdvancesRing) {  // the conv state becomes the last K-1 rows of [conv state ; rows]
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         if (j < K - 1) st(ring, (size_t)j * C + c, win[3 - (K - 1) + j]);
     }
   }
   if (tid < MAXR * G && gr < nrows) {
-    s_a[gr][gs] = ga;
-    s_b[gr][gs] = gb;
+    s_a[gr][gs] = p.gates_raw ? decay_from_raw(ga) : ga;
+    s_b[gr][gs] = p.gates_raw ? strength_from_raw(gb) : gb;
   }
-  if (tid < MAXR) s_dst[tid] = (MAXR > 1 && tid < nrows - 1) ? dst_mid : dst_last;
+  if (kStoresEveryRow && tid < MAXR) s_dst[tid] = tid < nrows - 1 ? dst_mid : dst_last;
   if (has_z && tid < G * D) {
     const float nwv = (float)rnw;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r)
-      if (r < nrows) s_zw[r][tid] = silu((float)rz[r]) * nwv;
+      if (r < nrows) {
+        const float zv = (float)rz[r];
+        s_zw[r][tid] = (p.norm_sigmoid ? __builtin_amdgcn_rcpf(1.0f + __expf(-zv)) : silu(zv)) * nwv;
+      }
   }
   __syncthreads();
 
@@ -220,7 +279,11 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   // issues only stores, and no wait inside it makes a row wait for the previous
   // row's state stores to complete.
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  floatx4 st_reg[RPT];
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) st_reg[rr] = StateIO<TS>::widen(st_raw[rr]);
   const int wv = t / kWave, lane = t % kWave;
+  const int stash_u = Hk * D + h * D, stash_a = Hk * D + Hv * D + g * G;
   for (int r = 0; r < nrows; ++r) {
     const float *qh = &s_qkv[r][0];
     const float *kh = &s_qkv[r][D];
@@ -250,20 +313,24 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
     }
     const float av = s_a[r][s], bv = s_b[r][s];
     const float4 v = *reinterpret_cast<const float4 *>(&s_qkv[r][2 * D + s * D + 4 * cq]);
-    float4 u;
+    floatx4 u;
     u.x = bv * (v.x - av * kv.x); u.y = bv * (v.y - av * kv.y);
     u.z = bv * (v.z - av * kv.z); u.w = bv * (v.w - av * kv.w);
 
-    gptr<float> dst = to_global(s_dst[r]) + (size_t)h * D * D;
+    const bool store_now = kStoresEveryRow || (kStoresLast && r == nrows - 1);
+    gptr<TS> dst = to_global(kStoresEveryRow ? s_dst[r] : dst_last) + (size_t)h * D * D;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const int row = rr * RG + rg;
-      const float kk = kh[row];
-      floatx4 nv;
-      nv.x = av * st_reg[rr].x + kk * u.x; nv.y = av * st_reg[rr].y + kk * u.y;
-      nv.z = av * st_reg[rr].z + kk * u.z; nv.w = av * st_reg[rr].w + kk * u.w;
+      const floatx4 nv = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, kh[row], u));
       st_reg[rr] = nv;
-      *reinterpret_cast<gptr<floatx4>>(dst + (size_t)row * D + 4 * cq) = nv;
+      if (store_now) StateIO<TS>::store(dst + (size_t)row * D + 4 * cq, nv);
+    }
+    if (MODE == kModeWoa) {  // stash row r0 + r: k_hat of the key head, u and a of the value heads
+      gptr<float> srow = to_global(p.stash) + (size_t)(r0 + r) * p.stash_row;
+      if (rg == 0) *reinterpret_cast<gptr<floatx4>>(srow + stash_u + 4 * cq) = u;
+      if (tid < CQ) *reinterpret_cast<gptr<floatx4>>(srow + g * D + 4 * tid) = *reinterpret_cast<const floatx4 *>(&kh[4 * tid]);
+      if (tid < G) srow[stash_a + tid] = s_a[r][tid];
     }
 
     if (rg == 0) {  // lanes 0..CQ-1 of the slot's first wave hold the head's outputs
@@ -279,111 +346,57 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
         const float4 zw = *reinterpret_cast<const float4 *>(&s_zw[r][s * D + 4 * cq]);
         o[0] *= inv * zw.x; o[1] *= inv * zw.y; o[2] *= inv * zw.z; o[3] *= inv * zw.w;
       }
-      store4(static_cast<TO *>(p.out) + obase, o);
+      if (p.geo.out_bf16)
+        store4(static_cast<bf16 *>(p.out) + obase, o);
+      else
+        store4(static_cast<float *>(p.out) + obase, o);
     }
   }
 }
 
-// Commit: copy the state after the last accepted row into table 0 and advance the
-// conv state over the accepted rows.  blockIdx.y < kCommitSplit: one eighth of the
-// state copy, 8 loads in flight per thread; otherwise conv-state channels.
-constexpr int kCommitSplit = 8;
-
-template <typename TE>
-__global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4) {
-  const int i = blockIdx.x;
-  const int k = p.cu[i + 1] - p.cu[i];
-  const int na = p.n_accepted[i];
-  if (na < 1 || na > k) return;  // outside the caller's contract: sequence untouched
-  if ((int)blockIdx.y < kCommitSplit) {
-    if (na == k) return;  // table 0 already holds the last state
-    // (native 4-float vectors: the struct-based float4 array ends up in scratch)
-    const gptr<const floatx4> src = to_global(reinterpret_cast<const floatx4 *>(p.tables[na * kTableSeqs + i]));
-    const gptr<floatx4> dst = to_global(reinterpret_cast<floatx4 *>(p.tables[i]));
-    const int64_t per = (n4 + kCommitSplit - 1) / kCommitSplit;
-    const int64_t beg = (int64_t)blockIdx.y * per, end = min(n4, beg + per);
-    // whole tiles of 256 x 8 float4 without conditions, then the tail
-    int64_t i0 = beg;
-    for (; i0 + 256 * 8 <= end; i0 += 256 * 8) {
-      floatx4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[i0 + threadIdx.x + u * 256];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) dst[i0 + threadIdx.x + u * 256] = v[u];
-    }
-    for (int64_t idx = i0 + threadIdx.x; idx < end; idx += 256) dst[idx] = src[idx];
-  } else {
-    const int C = p.geo.conv_dim, R = p.geo.K - 1;
-    const int c = ((int)blockIdx.y - kCommitSplit) * 256 + threadIdx.x;
-    if (c >= C) return;
-    TE *ring = static_cast<TE *>(p.conv_state[i]);
-    const TE *x = static_cast<const TE *>(p.x) + (size_t)p.cu[i] * C;
-    TE vals[3];
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {  // position na + r of [old conv state ; accepted rows]
-      const int idx = na + min(r, R - 1);
-      const TE vr = ring[(size_t)min(idx, R - 1) * C + c], vx = x[(size_t)max(idx - R, 0) * C + c];
-      vals[r] = (idx < R) ? vr : vx;
-    }
-#pragma unroll
-    for (int r = 0; r < 3; ++r)
-      if (r < R) ring[(size_t)r * C + c] = vals[r];
-  }
-}
-
-template <int D, int G, int MAXR, typename TA>
-hipError_t launch_rec_to(const RecurrentLaunch &p, hipStream_t stream) {
+// Launch of one mode over the supported shapes: D in {32, 64, 128}, H_v / H_k in
+// {1, 2, 4}, activations fp32 or bf16, states fp32 or binary16.
+template <int D, int G, int MAXR, int MODE, typename TA>
+hipError_t launch_rec_ts(const RecurrentLaunch &p, hipStream_t stream) {
   const dim3 grid(p.n * p.geo.Hk), block(kSlot * G);
-  if (p.geo.out_bf16)
-    hipLaunchKernelGGL((recurrent_kernel<D, G, MAXR, TA, bf16>), grid, block, 0, stream, p);
+  if (p.state_f16)
+    hipLaunchKernelGGL((recurrent_kernel<D, G, MAXR, MODE, TA, _Float16>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((recurrent_kernel<D, G, MAXR, TA, float>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((recurrent_kernel<D, G, MAXR, MODE, TA, float>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G, int MAXR>
+template <int D, int G, int MAXR, int MODE>
 hipError_t launch_rec_ta(const RecurrentLaunch &p, hipStream_t stream) {
-  return p.geo.act_bf16 ? launch_rec_to<D, G, MAXR, bf16>(p, stream)
-                        : launch_rec_to<D, G, MAXR, float>(p, stream);
+  return p.geo.act_bf16 ? launch_rec_ts<D, G, MAXR, MODE, bf16>(p, stream)
+                        : launch_rec_ts<D, G, MAXR, MODE, float>(p, stream);
 }
 
-template <int D, int G>
-hipError_t launch_rec_mode(const RecurrentLaunch &p, hipStream_t stream) {
-  return p.verify ? launch_rec_ta<D, G, 16>(p, stream) : launch_rec_ta<D, G, 1>(p, stream);
-}
-
-template <int D>
+template <int D, int MAXR, int MODE>
 hipError_t launch_rec_g(const RecurrentLaunch &p, hipStream_t stream) {
   switch (p.geo.Hv / p.geo.Hk) {
-    case 1: return launch_rec_mode<D, 1>(p, stream);
-    case 2: return launch_rec_mode<D, 2>(p, stream);
-    case 4: return launch_rec_mode<D, 4>(p, stream);
+    case 1: return launch_rec_ta<D, 1, MAXR, MODE>(p, stream);
+    case 2: return launch_rec_ta<D, 2, MAXR, MODE>(p, stream);
+    case 4: return launch_rec_ta<D, 4, MAXR, MODE>(p, stream);
   }
   return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-hipError_t launch_recurrent(const RecurrentLaunch &p, hipStream_t stream) {
+template <int MAXR, int MODE>
+hipError_t launch_rec_mode(const RecurrentLaunch &p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;
   switch (p.geo.D) {
-    case 32: return launch_rec_g<32>(p, stream);
-    case 64: return launch_rec_g<64>(p, stream);
-    case 128: return launch_rec_g<128>(p, stream);
+    case 32: return launch_rec_g<32, MAXR, MODE>(p, stream);
+    case 64: return launch_rec_g<64, MAXR, MODE>(p, stream);
+    case 128: return launch_rec_g<128, MAXR, MODE>(p, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_commit(const CommitLaunch &p, hipStream_t stream) {
-  if (p.n == 0) return hipSuccess;
-  const int64_t n4 = (int64_t)p.geo.Hv * p.geo.D * p.geo.D / 4;
-  const int nblk_ring = (p.geo.conv_dim + 255) / 256;
-  const dim3 grid(p.n, kCommitSplit + nblk_ring), block(256);
-  if (p.geo.act_bf16)
-    hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, n4);
-  else
-    hipLaunchKernelGGL((commit_kernel<float>), grid, block, 0, stream, p, n4);
-  return hipGetLastError();
-}
+// One translation unit per mode defines its launcher.
+hipError_t launch_rec_decode(const RecurrentLaunch &p, hipStream_t stream);
+hipError_t launch_rec_tokens(const RecurrentLaunch &p, hipStream_t stream);
+hipError_t launch_rec_verify(const RecurrentLaunch &p, hipStream_t stream);
+hipError_t launch_rec_woa(const RecurrentLaunch &p, hipStream_t stream);
 
 }  // namespace gdn

@@ -11,6 +11,11 @@ DEV = "cuda:0"
 # max|gpu - ref| / max|ref| over that slice.
 TOL_OUT = 2e-3      # outputs computed from bf16 (or fp32) inputs, compared in fp32
 TOL_STATE = 1e-4    # fp32 recurrent states
+# binary16 states: both sides round every stored state to nearest even, so they
+# differ only where the fp32 and the fp64 value of an element fall on different
+# sides of a rounding boundary -- one binary16 ulp of that element, at most
+# 2^-10 of the slice's largest magnitude; two such flips are allowed.
+TOL_STATE_F16 = 2.0 ** -9
 
 
 def tdev(a, dtype):
@@ -54,8 +59,8 @@ class DeviceStates:
     """Per-sequence fp32 states [Hv, dk, dv] and conv states [K-1, conv_dim] as
     separate device buffers reached through pointer arrays (pool-slot style)."""
 
-    def __init__(self, S0, ring, act):
-        self.h = [tdev(S0[i], torch.float32) for i in range(S0.shape[0])]
+    def __init__(self, S0, ring, act, state_dtype=torch.float32):
+        self.h = [tdev(S0[i], state_dtype) for i in range(S0.shape[0])]
         self.ring = [tdev(ring[i], act) for i in range(ring.shape[0])]
         self.h_ptrs = B.ptr_array(self.h) if self.h else torch.zeros(0, dtype=torch.int64, device=DEV)
         self.ring_ptrs = B.ptr_array(self.ring) if self.ring else torch.zeros(0, dtype=torch.int64, device=DEV)
@@ -65,3 +70,9 @@ class DeviceStates:
 
     def ring_host(self):
         return np.stack([host(t) for t in self.ring])
+
+
+def f16_exact(a):
+    """The nearest binary16 values of an fp32 array, as fp32 (a state stored as
+    binary16 is handed to the oracle as exactly these values)."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)

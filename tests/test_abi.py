@@ -24,6 +24,7 @@ def test_library_exports_every_declared_symbol():
     names = _declared_functions()
     assert {"gdn_conv_l2norm", "gdn_prefill_chunked", "gdn_decode_batched", "gdn_verify_multi",
             "gdn_verify_commit", "gdn_gated_rmsnorm", "gdn_prefill_workspace_bytes",
+            "gdn_verify_woa", "gdn_woa_stash_bytes", "gdn_fold_accepted", "gdn_decode_tokens",
             "gdn_status_string", "gdn_abi_version"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -31,12 +32,13 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert n in exported, n
         assert hasattr(B.library(), n)
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
 
 
 def test_struct_layout_matches_header(tmp_path):
-    structs = ["gdn_dims", "gdn_conv_args", "gdn_prefill_args", "gdn_decode_args", "gdn_verify_args",
-               "gdn_commit_args", "gdn_norm_args"]
+    structs = ["gdn_dims", "gdn_options", "gdn_conv_args", "gdn_prefill_args", "gdn_decode_args",
+               "gdn_verify_args", "gdn_commit_args", "gdn_norm_args", "gdn_woa_args", "gdn_fold_args",
+               "gdn_tokens_args"]
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gdn.h"', "int main(void) {"]
     for s in structs:
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (s, s))
@@ -195,3 +197,93 @@ def test_prefill_validation_and_workspace():
     assert _ws(_prefill_args(dims=_dims(d=80)))[0] == B.GDN_ERR_UNSUPPORTED
     ok = _prefill_args(num_seqs=0, total_tokens=0)
     assert L.gdn_prefill_chunked(ctypes.byref(ok), None) == B.GDN_OK
+
+
+def test_options_are_refused_where_not_taken():
+    """Every entry point validates its options before any launch: an unknown value,
+    the reserved word, or an option the entry point does not take."""
+    F16, RAW, SIG = B.GDN_DTYPE_F16, B.GDN_GATES_RAW, B.GDN_NORM_GATE_SIGMOID
+    # decode takes all three: an unknown value or the bf16 "state" is refused
+    assert _decode(opt=B.gdn_options(B.GDN_DTYPE_BF16, 0, 0, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _decode(opt=B.gdn_options(0, 2, 0, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _decode(opt=B.gdn_options(0, 0, 2, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _decode(opt=B.gdn_options(0, 0, 0, 1)) == B.GDN_ERR_INVALID_ARG
+    assert _decode(num_seqs=0, opt=B.gdn_options(F16, RAW, SIG, 0)) == B.GDN_OK
+    assert _verify(num_seqs=0, total_rows=0, opt=B.gdn_options(F16, RAW, SIG, 0)) == B.GDN_OK
+    # commit takes only the state dtype, the norm only the norm gate
+    assert _commit(num_seqs=0, opt=B.gdn_options(F16, 0, 0, 0)) == B.GDN_OK
+    assert _commit(opt=B.gdn_options(0, RAW, 0, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _commit(opt=B.gdn_options(0, 0, SIG, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _norm(total_tokens=0, o=None, opt=B.gdn_options(0, 0, SIG, 0)) == B.GDN_OK
+    assert _norm(opt=B.gdn_options(F16, 0, 0, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _norm(opt=B.gdn_options(0, RAW, 0, 0)) == B.GDN_ERR_INVALID_ARG
+    ok = _prefill_args(num_seqs=0, total_tokens=0, opt=B.gdn_options(F16, RAW, SIG, 0))
+    assert B.library().gdn_prefill_chunked(ctypes.byref(ok), None) == B.GDN_OK
+
+
+def _woa_args(**kw):
+    a = B.gdn_woa_args(struct_size=ctypes.sizeof(B.gdn_woa_args), act_dtype=1, out_dtype=1, dims=_dims(),
+                       num_seqs=64, max_k=16, total_rows=576, cu_ks=FAKE, x=FAKE, conv_w=FAKE,
+                       conv_state=FAKE, a=FAKE, b=FAKE, h_state=FAKE, out=FAKE, stash=FAKE,
+                       stash_bytes=0, scale=1.0, l2_eps=1e-6, norm_eps=1e-6)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_woa_validation_and_stash_size():
+    L = B.library()
+    n = ctypes.c_size_t(0)
+    assert L.gdn_woa_stash_bytes(ctypes.byref(_woa_args()), ctypes.byref(n)) == B.GDN_OK
+    # per row: k_hat of 16 key heads, u and a of 32 value heads (16*128 + 32*128 + 32 floats)
+    assert n.value == 576 * (16 * 128 + 32 * 128 + 32) * 4
+    n2 = ctypes.c_size_t(0)
+    assert L.gdn_woa_stash_bytes(ctypes.byref(_woa_args(dims=B.gdn_dims(1, 1, 32, 32, 4, 0), total_rows=3)),
+                                 ctypes.byref(n2)) == B.GDN_OK
+    assert n2.value == 3 * 68 * 4  # 32 + 32 + 1 floats, rounded up to 68
+    run = lambda **kw: L.gdn_verify_woa(ctypes.byref(_woa_args(**kw)), None)
+    assert run() == B.GDN_ERR_WORKSPACE
+    assert run(stash_bytes=n.value - 4) == B.GDN_ERR_WORKSPACE
+    assert run(stash=None, stash_bytes=n.value) == B.GDN_ERR_WORKSPACE
+    assert run(max_k=17, stash_bytes=n.value) == B.GDN_ERR_INVALID_ARG
+    assert run(num_seqs=129, stash_bytes=n.value) == B.GDN_ERR_INVALID_ARG
+    assert run(h_state=None, stash_bytes=n.value) == B.GDN_ERR_INVALID_ARG
+    assert run(reserved_f=1.0, stash_bytes=n.value) == B.GDN_ERR_INVALID_ARG
+    assert run(num_seqs=0, total_rows=0, stash=None) == B.GDN_OK
+
+
+def _fold(**kw):
+    a = B.gdn_fold_args(struct_size=ctypes.sizeof(B.gdn_fold_args), act_dtype=1, dims=_dims(), num_seqs=64,
+                        total_rows=576, cu_ks=FAKE, n_accepted=FAKE, h_state=FAKE, stash=FAKE,
+                        stash_bytes=576 * 6176 * 4, x=FAKE, conv_state=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_fold_accepted(ctypes.byref(a), None)
+
+
+def test_fold_validation():
+    assert _fold(stash_bytes=576 * 6176 * 4 - 1) == B.GDN_ERR_WORKSPACE
+    assert _fold(n_accepted=None) == B.GDN_ERR_INVALID_ARG
+    assert _fold(num_seqs=129) == B.GDN_ERR_INVALID_ARG
+    assert _fold(opt=B.gdn_options(0, B.GDN_GATES_RAW, 0, 0)) == B.GDN_ERR_INVALID_ARG
+    assert _fold(num_seqs=0, opt=B.gdn_options(B.GDN_DTYPE_F16, 0, 0, 0)) == B.GDN_OK
+
+
+def _tokens(**kw):
+    a = B.gdn_tokens_args(struct_size=ctypes.sizeof(B.gdn_tokens_args), act_dtype=1, out_dtype=1, dims=_dims(),
+                          num_seqs=8, max_tokens=17, total_rows=100, cu_tokens=FAKE, x=FAKE, conv_w=FAKE,
+                          conv_state=FAKE, a=FAKE, b=FAKE, h_state=FAKE, out=FAKE, scale=1.0, l2_eps=1e-6,
+                          norm_eps=1e-6)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return B.library().gdn_decode_tokens(ctypes.byref(a), None)
+
+
+def test_tokens_validation():
+    assert _tokens(max_tokens=18) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(max_tokens=0) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(total_rows=8 * 17 + 1) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(num_seqs=129) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(cu_tokens=None) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(z=FAKE) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(num_seqs=0, total_rows=0) == B.GDN_OK
