@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4)
 // Fold: blockIdx.y < H_v is one value head's state, read once, advanced over the
 // accepted rows from the stash in order (the verify's rank-1 update, bit for bit),
 // and written once; the other blocks advance the conv state.  Thread t holds
-// column quad t % (D/4) of rows rr * (1024/D) + t / (D/4), as in the verify.
+// column quad t % (D/4) of the D^2/1024 consecutive rows from (t / (D/4)) D^2/1024,
+// as in the verify.
 template <int D, typename TE, typename TS>
 __global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
   constexpr int CQ = D / 4, RG = kSlot / CQ, RPT = D / RG;
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
   const gptr<TS> S = to_global(static_cast<TS *>(p.states[i])) + (size_t)h * D * D;
   typename StateIO<TS>::raw st_raw[RPT];
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S + (size_t)(rr * RG + rg) * D + 4 * cq);
+  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S + (size_t)(rg * RPT + rr) * D + 4 * cq);
   const gptr<const float> stash = to_global(p.stash) + (size_t)r0 * p.stash_row;
   for (int e = t; e < na * D; e += kSlot) {
     const int r = e / D, j = e - r * D;
@@ -103,10 +104,10 @@ __global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
     const floatx4 u = *reinterpret_cast<const floatx4 *>(&s_u[r][4 * cq]);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr)
-      st_reg[rr] = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, s_k[r][rr * RG + rg], u));
+      st_reg[rr] = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, s_k[r][rg * RPT + rr], u));
   }
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) StateIO<TS>::store(S + (size_t)(rr * RG + rg) * D + 4 * cq, st_reg[rr]);
+  for (int rr = 0; rr < RPT; ++rr) StateIO<TS>::store(S + (size_t)(rg * RPT + rr) * D + 4 * cq, st_reg[rr]);
 }
 
 template <int D, typename TE>

@@ -21,9 +21,10 @@
 // runs once and feeds the H_v/H_k value heads of the group through LDS, and
 // because one workgroup owns all channels of the group the in-place conv-state
 // update has no cross-workgroup race.  256 threads own one value head: thread t
-// holds column quad (t % 32) of rows {rr * 8 + t / 32}, so every wave-wide load or
-// store covers whole contiguous state rows, and the state stays in registers
-// across the rows of a sequence.  S k and S q are reduced over row groups with
+// holds column quad (t % 32) of the 16 consecutive rows 16 (t / 32) .. +15, so
+// every wave-wide load or store covers two whole 512-byte state rows, a thread's
+// share of k_hat and q_hat is four 16-byte LDS reads, and the state stays in
+// registers across the rows of a sequence.  S k and S q are reduced over row groups with
 // wave shuffles and one LDS exchange per row.  All arithmetic is fp32 (the
 // recurrence per token is
 //   kv = S k;  u = b (v - a kv);  S <- a S + u k^T;  o = scale (a S q + (k.q) u),
@@ -94,12 +95,31 @@ __device__ __forceinline__ void store4(bf16 *p, const float v[4]) {
   *reinterpret_cast<uint2 *>(p) = w.u;
 }
 
+// A pointer every lane holds the same value of (read from LDS, say), moved to
+// scalar registers: stores through it then take a scalar base address.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
 // Raw gate inputs: a = exp(-softplus(g)) = 1 / (1 + e^g), b = 1 / (1 + e^-beta).
 __device__ __forceinline__ float decay_from_raw(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(g)); }
 __device__ __forceinline__ float strength_from_raw(float beta) { return __builtin_amdgcn_rcpf(1.0f + __expf(-beta)); }
 
+// Waves per SIMD the kernel is compiled for: in the multi-row modes two workgroups
+// per CU (4 waves per SIMD at H_v/H_k = 2, <= 128 VGPRs) overlap one workgroup's
+// loads and row arithmetic with another's stores.
+template <int G, int MODE>
+constexpr int rec_waves_per_eu() {
+  return MODE == kModeDecode ? 1 : (G == 1 ? 2 : 4);
+}
+
 template <int D, int G, int MAXR, int MODE, typename TA, typename TS>
-__global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) {
+__global__ __launch_bounds__(kSlot *G) __attribute__((amdgpu_waves_per_eu(rec_waves_per_eu<G, MODE>())))
+void recurrent_kernel(RecurrentLaunch p) {
   constexpr int CQ = D / 4;            // column quads of a head
   constexpr int RG = kSlot / CQ;       // row groups
   constexpr int RPT = D / RG;          // state rows held by a thread
@@ -146,9 +166,11 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
       if (rk == rank) s_seq = t;
     }
     __syncthreads();
-    i = s_seq;
-    r0 = s_cu[i];
-    nrows = s_cu[i + 1] - r0;
+    // uniform over the block: read into scalar registers, so that every address
+    // derived from them is scalar too
+    i = __builtin_amdgcn_readfirstlane(s_seq);
+    r0 = __builtin_amdgcn_readfirstlane(s_cu[i]);
+    nrows = __builtin_amdgcn_readfirstlane(s_cu[i + 1]) - r0;
     nrows = nrows < 0 ? 0 : (nrows > MAXR ? MAXR : nrows);
   }
   if (nrows == 0) return;  // uniform over the block
@@ -198,15 +220,23 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
     rz[r] = zp[has_z ? (size_t)(r0 + min(r, nrows - 1)) * Hv * D + (size_t)g * G * D + zc : 0];
   const TA rnw = nwp[has_z ? zc % D : 0];
 
-  // ---- the state loads; the prologue's arithmetic hides their latency ---------
+  // ---- the state loads -------------------------------------------------------
+  // One-token decode issues them here, so the prologue's arithmetic hides their
+  // latency.  The multi-row modes issue them after the prologue has consumed its
+  // raw rows: the two sets of registers are then never live together, which keeps
+  // the kernel within the register budget of two workgroups per CU, and the other
+  // workgroup on the CU hides the latency instead.
   const int s = tid / kSlot, t = tid % kSlot;
   const int h = g * G + s;
   const int cq = t % CQ, rg = t / CQ;
   const gptr<const TS> S_in = to_global(static_cast<const TS *>(p.states[i])) + (size_t)h * D * D;
   typename StateIO<TS>::raw st_raw[RPT];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S_in + (size_t)(rr * RG + rg) * D + 4 * cq);
-  __builtin_amdgcn_sched_barrier(0);
+    for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S_in + (size_t)(rg * RPT + rr) * D + 4 * cq);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (MODE == kModeDecode) load_state();
 
   // ---- prologue: conv + SiLU of the group's channels for every row ----------
 #pragma unroll
@@ -272,6 +302,7 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
       if (lane == 0) s_qk[r] = dqk * iq * ik;
     }
   }
+  if constexpr (MODE != kModeDecode) load_state();
   __syncthreads();
 
   // ---- the recurrence, row by row --------------------------------------------
@@ -287,11 +318,24 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
   for (int r = 0; r < nrows; ++r) {
     const float *qh = &s_qkv[r][0];
     const float *kh = &s_qkv[r][D];
+    float kr[RPT], qr[RPT];  // this thread's rows of k_hat and q_hat
+    if constexpr (RPT % 4 == 0) {  // 16-byte aligned groups of 4 rows
+#pragma unroll
+      for (int j = 0; j < RPT; j += 4) {
+        *reinterpret_cast<floatx4 *>(&kr[j]) = *reinterpret_cast<const floatx4 *>(&kh[rg * RPT + j]);
+        *reinterpret_cast<floatx4 *>(&qr[j]) = *reinterpret_cast<const floatx4 *>(&qh[rg * RPT + j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        kr[j] = kh[rg * RPT + j];
+        qr[j] = qh[rg * RPT + j];
+      }
+    }
     float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
-      const int row = rr * RG + rg;
-      const float kk = kh[row], qq = qh[row];
+      const float kk = kr[rr], qq = qr[rr];
       pk.x += kk * st_reg[rr].x; pk.y += kk * st_reg[rr].y; pk.z += kk * st_reg[rr].z; pk.w += kk * st_reg[rr].w;
       pq.x += qq * st_reg[rr].x; pq.y += qq * st_reg[rr].y; pq.z += qq * st_reg[rr].z; pq.w += qq * st_reg[rr].w;
     }
@@ -318,13 +362,12 @@ __global__ __launch_bounds__(kSlot *G) void recurrent_kernel(RecurrentLaunch p) 
     u.z = bv * (v.z - av * kv.z); u.w = bv * (v.w - av * kv.w);
 
     const bool store_now = kStoresEveryRow || (kStoresLast && r == nrows - 1);
-    gptr<TS> dst = to_global(kStoresEveryRow ? s_dst[r] : dst_last) + (size_t)h * D * D;
+    gptr<TS> dst = to_global(kStoresEveryRow ? uniform_ptr(s_dst[r]) : dst_last) + (size_t)h * D * D;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
-      const int row = rr * RG + rg;
-      const floatx4 nv = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, kh[row], u));
+      const floatx4 nv = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, kr[rr], u));
       st_reg[rr] = nv;
-      if (store_now) StateIO<TS>::store(dst + (size_t)row * D + 4 * cq, nv);
+      if (store_now) StateIO<TS>::store(dst + (size_t)(rg * RPT + rr) * D + 4 * cq, nv);
     }
     if (MODE == kModeWoa) {  // stash row r0 + r: k_hat of the key head, u and a of the value heads
       gptr<float> srow = to_global(p.stash) + (size_t)(r0 + r) * p.stash_row;

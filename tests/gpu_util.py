@@ -37,6 +37,8 @@ def slice_err(gpu, ref, row_seq=None):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape
+    if not np.all(np.isfinite(gpu)):
+        return float("inf")  # a NaN or infinity anywhere fails every tolerance
     worst = 0.0
     if row_seq is None:
         diff = np.abs(gpu - ref).reshape(ref.shape[0], ref.shape[1], -1).max(axis=2)
