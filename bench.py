@@ -45,9 +45,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "82cda49abff4ac52f58802336ab7f48e0b8ccea66adebd435b32ea85608c46e9",
-    "fetch_kib": 136027.8, "write_kib": 269312.0,
-    "fetch_scale": 1048576.0 / 524302.1, "write_scale": 1048576.0 / 1048576.0,
+    "sha256": "48f5024d51d4ab2e6baf069aa7a551448f0b37ae6ce7e491ffdba8c2e8c3cfcc",
+    "fetch_kib": 136030.8, "write_kib": 269312.0,
+    "fetch_scale": 1048576.0 / 524302.0, "write_scale": 1048576.0 / 1048576.0,
 }
 
 
