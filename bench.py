@@ -301,6 +301,27 @@ def variant_phases(torch, B, W, w, reps=10):
     db = w.d_n * decode_bytes_per_seq() + CONV_DIM * 4 * 2 + D * 2
     res["decode_raw_gates_sigmoid_norm"] = {"ms_per_launch": msg, "gb_per_s": db / (msg / 1e3) / 1e9,
                                             "hbm_frac": db / (msg / 1e3) / HBM_PEAK}
+    # the varlen packed prefill: 8 sequences, log-uniform lengths, one call with the
+    # conv + L2 front and the gated-norm epilogue fused
+    p = W.config(4)
+    T4 = int(p["cu"][-1])
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+    cu4, x4, z4 = t(p["cu"], torch.int32), t(p["x"], bf), t(p["z"], bf)
+    a4, b4, w4, nw4 = t(p["a"], f32), t(p["b"], f32), t(p["conv_w"], bf), t(p["norm_w"], bf)
+    h4 = [t(p["S0"][i], f32) for i in range(p["S0"].shape[0])]
+    r4 = [t(p["ring"][i], bf) for i in range(p["ring"].shape[0])]
+    hp4, rp4 = B.ptr_array(h4), B.ptr_array(r4)
+    out4 = torch.empty((T4, HV * D), dtype=bf, device=dev)
+    kw4 = dict(x=x4, conv_w=w4, conv_state_ptrs=rp4, z=z4, norm_w=nw4)
+    ws4 = torch.empty(max(B.gdn_prefill_workspace_bytes(dims, cu4, a4, b4, hp4, out4, **kw4), 1), dtype=torch.uint8,
+                      device=dev)
+    ms4 = _timed(torch, lambda: B.gdn_prefill_chunked(dims, cu4, a4, b4, hp4, out4, workspace=ws4, **kw4), 3)
+    fl4 = prefill_flops_per_token() * T4
+    by4 = T4 * (CONV_DIM * 2 + 2 * HV * D * 2 + 2 * HV * 4) + len(h4) * 2 * STATE_BYTES
+    res["prefill_varlen_fused"] = {"tokens": T4, "sequences": len(h4), "longest": int(np.max(np.diff(p["cu"]))),
+                                   "ms": ms4, "tokens_per_s": T4 / (ms4 / 1e3),
+                                   "tflops": fl4 / (ms4 / 1e3) / 1e12, "mfma_frac": fl4 / (ms4 / 1e3) / MFMA_BF16_PEAK,
+                                   "hbm_frac": by4 / (ms4 / 1e3) / HBM_PEAK}
     return res
 
 

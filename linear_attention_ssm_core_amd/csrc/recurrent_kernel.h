@@ -260,8 +260,13 @@ void recurrent_kernel(RecurrentLaunch p) {
     }
     if (kAdvancesRing) {  // the conv state becomes the last K-1 rows of [conv state ; rows]
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        if (j < K - 1) st(ring, (size_t)j * C + c, win[3 - (K - 1) + j]);
+      for (int j = 0; j < 3; ++j) {
+        // row j of the new state is win[j + 4 - K]; selected with constant indices (a
+        // register array indexed by the run-time K would live in scratch memory)
+        const int idx = j + 4 - K;
+        const float v = idx == 0 ? win[0] : (idx == 1 ? win[1] : win[2]);
+        if (j < K - 1) st(ring, (size_t)j * C + c, v);
+      }
     }
   }
   if (tid < MAXR * G && gr < nrows) {

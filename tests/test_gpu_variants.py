@@ -48,7 +48,7 @@ def _stash_parts(stash, T, dims):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("case,state", [("config3", "f32"), ("config3", "f16"), ("tiny_fp32", "f32"),
-                                        ("edge_k", "f32")])
+                                        ("edge_k", "f32"), ("n128_k1", "f32"), ("d64_g4", "f16")])
 def test_woa_verify_and_fold(case, state):
     """Outputs and stash against the oracle; the fold of the accepted rows against
     the oracle, and bit for bit against the state the write-all verify records
@@ -59,10 +59,17 @@ def test_woa_verify_and_fold(case, state):
     elif case == "tiny_fp32":
         d = W.verify_inputs(3101, 5, W.TINY_DIMS, act="f32")
         sample = np.arange(5)
-    else:  # k = 2 and 16 only, accepted n = 1 and n = k
+    elif case == "edge_k":  # k = 2 and 16 only, accepted n = 1 and n = k
         d = W.verify_inputs(3102, 6, W.QWEN_DIMS, ks=[2, 16, 2, 16, 16, 2])
         d["n_acc"] = np.array([1, 16, 2, 1, 7, 2], dtype=np.int32)
         sample = np.arange(6)
+    elif case == "n128_k1":  # the widest batch, with one-row sequences among 16-row ones
+        ks = np.array(([1, 16, 5, 1] * 32)[:128])
+        d = W.verify_inputs(3111, 128, W.QWEN_DIMS, ks=ks)
+        sample = np.array([0, 1, 2, 3, 64, 126, 127])
+    else:  # d = 64, four value heads per key head
+        d = W.verify_inputs(3112, 7, W.Dims(Hk=2, Hv=8, dk=64, dv=64, K=4), act="bf16")
+        sample = np.arange(7)
     sdt = torch.float16 if state == "f16" else torch.float32
     if state == "f16":
         d["S0"] = f16_exact(d["S0"])
@@ -277,7 +284,7 @@ def test_raw_gates_and_sigmoid_norm_prefill():
 # several consecutive tokens per sequence
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state"])
+@pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state", "n128"])
 def test_decode_tokens(case):
     """k_i tokens per sequence (1..17) against the oracle's token-by-token decode;
     the final state equals, bit for bit, the last state the verify stores for the
@@ -288,10 +295,13 @@ def test_decode_tokens(case):
     elif case == "k17_tiny_fp32":
         ks = [17, 17, 4]
         d = W.verify_inputs(3109, len(ks), W.TINY_DIMS, act="f32", ks=ks)
-    else:
+    elif case == "f16_state":
         ks = [12, 7, 1, 16]
         d = W.verify_inputs(3110, len(ks), W.QWEN_DIMS, ks=ks)
         d["S0"] = f16_exact(d["S0"])
+    else:  # the widest batch, k = 1 and 17 alternating, d = 64 heads
+        ks = [1, 17] * 64
+        d = W.verify_inputs(3113, len(ks), W.Dims(Hk=4, Hv=8, dk=64, dv=64, K=4), ks=ks)
     state = "f16" if case == "f16_state" else "f32"
     sdt = torch.float16 if state == "f16" else torch.float32
     dims, act = d["dims"], act_dtype(d)
@@ -324,3 +334,28 @@ def test_decode_tokens(case):
     for j, i in enumerate(keep):
         assert torch.equal(ds.h[i], ds2.h[j]), i
     assert torch.equal(out[torch.from_numpy(rows).to(DEV)], out2)
+
+
+def test_extreme_raw_gates_and_f16_shapes():
+    """Raw gate inputs at +-30 (a and b saturating towards 0 and 1) with binary16
+    states at d = 32 and d = 64 and one or four value heads per key head."""
+    for dims, seed in ((W.Dims(Hk=4, Hv=4, dk=32, dv=32, K=4), 3114), (W.Dims(Hk=2, Hv=8, dk=64, dv=64, K=3), 3115)):
+        d = W.decode_inputs(seed, 6, 3, dims)
+        d["S0"] = f16_exact(d["S0"])
+        rng = np.random.default_rng(seed)
+        ds = DeviceStates(d["S0"], d["ring"], torch.bfloat16, torch.float16)
+        S, ring = d["S0"].astype(np.float64), d["ring"].astype(np.float64)
+        opt = B.options(torch.float16, gates="raw", norm_gate="sigmoid")
+        for step in range(3):
+            g = rng.choice([-30.0, -3.0, 0.0, 3.0, 30.0], size=d["a"][step].shape).astype(np.float32)
+            beta = rng.choice([-30.0, 0.0, 30.0], size=d["b"][step].shape).astype(np.float32)
+            out = torch.empty((6, dims.Hv * dims.dv), dtype=torch.float32, device=DEV)
+            B.gdn_decode_batched(tdev(d["x"][step], torch.bfloat16), tdev(d["conv_w"], torch.bfloat16), ds.ring_ptrs,
+                                 tdev(g, torch.float32), tdev(beta, torch.float32), ds.h_ptrs, out, dims,
+                                 z=tdev(d["z"][step], torch.bfloat16), norm_w=tdev(d["norm_w"], torch.bfloat16), opt=opt)
+            r = oracle.decode(d["x"][step], d["conv_w"], ring, g, beta, S, dims.Hk, dims.Hv, dims.dk, dims.dv,
+                              z=d["z"][step], norm_w=d["norm_w"], gates="raw", norm_gate="sigmoid", state="f16")
+            S, ring = r["S"], r["ring"]
+            assert slice_err(host(out).reshape(6, dims.Hv, dims.dv), r["out"], np.arange(6)) < TOL_OUT
+        assert slice_err(ds.h_host(), S) < TOL_STATE_F16
+        assert np.array_equal(ds.ring_host(), ring)
