@@ -273,15 +273,27 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     Gam[lane] = expf(la);
   }
   // K rows for the K^T staging of phase D: lane = token, 8 consecutive columns
-  // per load (columns 8 (wave + 4 m) ..), written to LDS only once Abar is dead
+  // per load (columns 8 (wave + 4 m) ..), written to LDS only once Abar is dead.
+  // With fp32 activations every operand is a hi/lo pair: holding all of them from
+  // here on would take the whole register file (one workgroup per CU), so those
+  // staging rows are loaded in phase D and the K tiles of phase B one at a time.
   bf16x8 kth[NIG], ktl[NIG];
+  auto load_kt = [&]() {
 #pragma unroll
-  for (int m = 0; m < NIG; ++m) frag8(Kb + (size_t)min(lane, L - 1) * CD + 8 * (wave + 4 * m), kth[m], ktl[m]);
+    for (int m = 0; m < NIG; ++m) frag8(Kb + (size_t)min(lane, L - 1) * CD + 8 * (wave + 4 * m), kth[m], ktl[m]);
+  };
+  if constexpr (!SP) load_kt();
   // wave w owns row block w of Q K^T -> M and of K K^T -> Abar.  (Its own K rows
   // are loaded on their own: picking them out of kh by the wave index would be a
   // run-time index into a register array, i.e. scratch memory.)
   const int ti = wave;
-  bf16x8 qh[KS], ql[KS], kih[KS], kil[KS], kh[4][KS], kl[4][KS];
+  constexpr int NKT = SP ? 1 : 4;  // K tiles held at once
+  bf16x8 qh[KS], ql[KS], kih[KS], kil[KS], kh[NKT][KS], kl[NKT][KS];
+  auto load_ktile = [&](int tj, int slot) {
+    const TY *krow = Kb + (size_t)min(16 * tj + lr, L - 1) * CD + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) frag8(krow + 32 * ks, kh[slot][ks], kl[slot][ks]);
+  };
   {
     const TY *qrow = Qb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
     const TY *kirow = Kb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
@@ -290,11 +302,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       frag8(qrow + 32 * ks, qh[ks], ql[ks]);
       frag8(kirow + 32 * ks, kih[ks], kil[ks]);
     }
+    if constexpr (!SP) {
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      const TY *krow = Kb + (size_t)min(16 * tj + lr, L - 1) * CD + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) frag8(krow + 32 * ks, kh[tj][ks], kl[tj][ks]);
+      for (int tj = 0; tj < 4; ++tj) load_ktile(tj, tj);
     }
   }
   __syncthreads();
@@ -305,10 +315,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   for (int tj = 0; tj < 4; ++tj) {
     floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti) {
+      const int slot = SP ? 0 : tj;
+      if constexpr (SP) load_ktile(tj, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        aq = mma<SP, SP>(aq, qh[ks], ql[ks], kh[tj][ks], kl[tj][ks]);
-        ak = mma<SP, SP>(ak, kih[ks], kil[ks], kh[tj][ks], kl[tj][ks]);
+        aq = mma<SP, SP>(aq, qh[ks], ql[ks], kh[slot][ks], kl[slot][ks]);
+        ak = mma<SP, SP>(ak, kih[ks], kil[ks], kh[slot][ks], kl[slot][ks]);
       }
     }
 #pragma unroll
@@ -382,6 +394,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   // ---- D: T = L^-1 diag(b); MT = M T and E = K^T diag(D) T on MFMA ----
   // Wave w owns rows j in [16w, 16w + 16) of T^T; its A operands are columns of T,
   // read now, before L^-1's region is reused for M.
+  if constexpr (SP) load_kt();
   const int jrow = 16 * wave + lr;
   const float bj = s_bb[jrow];
   bf16x8 th[2], tl[2], dh[2], dl[2];
