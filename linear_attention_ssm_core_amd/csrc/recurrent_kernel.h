@@ -105,6 +105,11 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
   return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
 }
 
+// Gate of the fused norm: SiLU(z) or sigmoid(z).
+__device__ __forceinline__ float norm_gate(float z, int sigmoid) {
+  return sigmoid ? __builtin_amdgcn_rcpf(1.0f + __expf(-z)) : silu(z);
+}
+
 // Raw gate inputs: a = exp(-softplus(g)) = 1 / (1 + e^g), b = 1 / (1 + e^-beta).
 __device__ __forceinline__ float decay_from_raw(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(g)); }
 __device__ __forceinline__ float strength_from_raw(float beta) { return __builtin_amdgcn_rcpf(1.0f + __expf(-beta)); }
@@ -112,13 +117,15 @@ __device__ __forceinline__ float strength_from_raw(float beta) { return __builti
 // Waves per SIMD the kernel is compiled for: in the multi-row modes two workgroups
 // per CU (4 waves per SIMD at H_v/H_k = 2, <= 128 VGPRs) overlap one workgroup's
 // loads and row arithmetic with another's stores.
-template <int G, int MODE>
+template <int G, int MODE, int STATE_BYTES>
 constexpr int rec_waves_per_eu() {
-  return MODE == kModeDecode ? 1 : (G == 1 ? 2 : 4);
+  // (the binary16 verify keeps its default: at 128 VGPRs it would spill inside the
+  // row loop, and a reload there waits for every store still in flight)
+  return (MODE == kModeDecode || (MODE == kModeVerify && STATE_BYTES == 2)) ? 1 : (G == 1 ? 2 : 4);
 }
 
 template <int D, int G, int MAXR, int MODE, typename TA, typename TS>
-__global__ __launch_bounds__(kSlot *G) __attribute__((amdgpu_waves_per_eu(rec_waves_per_eu<G, MODE>())))
+__global__ __launch_bounds__(kSlot *G) __attribute__((amdgpu_waves_per_eu(rec_waves_per_eu<G, MODE, sizeof(TS)>())))
 void recurrent_kernel(RecurrentLaunch p) {
   constexpr int CQ = D / 4;            // column quads of a head
   constexpr int RG = kSlot / CQ;       // row groups
@@ -128,15 +135,30 @@ void recurrent_kernel(RecurrentLaunch p) {
   constexpr bool kStoresEveryRow = MODE == kModeVerify;
   constexpr bool kStoresLast = MODE == kModeDecode || MODE == kModeTokens;
   constexpr bool kAdvancesRing = MODE == kModeDecode || MODE == kModeTokens;
+  // Write-on-accept verify and k-token decode: a wave holds every row group of its
+  // CQW column quads, so the per-row reductions are shuffles within the wave and
+  // the row loop has no barrier (the fused norm, which needs a whole head, runs
+  // after the loop).  The one-token decode and the verify that stores every state
+  // keep a wave over 2 row groups x all column quads: their stores then cover whole
+  // 512-byte rows, which the HBM write stream takes faster than 128-byte pieces.
+  constexpr bool kInWave = MODE == kModeWoa || MODE == kModeTokens;
+  constexpr int CQW = CQ / 4;  // column quads per wave (in-wave layout)
+  // Multi-row modes apply the fused norm after the row loop (one wave per row and
+  // value head), the same code for both layouts; together with reductions of the
+  // same association (a butterfly over row groups in the in-wave layout, pairs of
+  // wave partials in the other) every multi-row mode produces bit-identical
+  // outputs and update vectors, so a fold of the stash equals the recorded states.
+  constexpr bool kPostNorm = MODE != kModeDecode;
   static_assert(RPT * RG == D, "head dim must split over the row groups");
   static_assert((MODE == kModeDecode) == (MAXR == 1), "one-token decode is the MAXR = 1 instance");
 
   __shared__ float s_qkv[MAXR][NCH];
   __shared__ float s_a[MAXR][G], s_b[MAXR][G];
   __shared__ float s_qk[MAXR];
-  __shared__ float s_zw[MAXR][G * D];  // gate(z) * norm weight of the group's value channels
+  __shared__ float s_zw[kPostNorm ? 1 : MAXR][G * D];  // gate(z) * norm weight (decode)
   __shared__ TS *s_dst[kStoresEveryRow ? MAXR : 1];  // verify: where the state after each row goes
-  __shared__ float4 s_red[2][G][4][CQ][2];
+  __shared__ float4 s_red[kInWave ? 1 : 2][G][4][CQ][2];
+  __shared__ float s_o[kPostNorm ? MAXR : 1][G * D];  // pre-norm outputs (multi-row modes, with z)
 
   const int Hk = p.geo.Hk, Hv = p.geo.Hv, K = p.geo.K, C = p.geo.conv_dim;
   const int rank = blockIdx.x / Hk;
@@ -214,9 +236,10 @@ void recurrent_kernel(RecurrentLaunch p) {
   const TA *zp = has_z ? static_cast<const TA *>(p.z) : x;
   const TA *nwp = has_z ? static_cast<const TA *>(p.norm_w) : x;
   const int zc = min(tid, G * D - 1);
-  TA rz[MAXR];
+  constexpr int NZ = kPostNorm ? 1 : MAXR;  // z rows staged by the prologue (decode)
+  TA rz[NZ];
 #pragma unroll
-  for (int r = 0; r < MAXR; ++r)
+  for (int r = 0; r < NZ; ++r)
     rz[r] = zp[has_z ? (size_t)(r0 + min(r, nrows - 1)) * Hv * D + (size_t)g * G * D + zc : 0];
   const TA rnw = nwp[has_z ? zc % D : 0];
 
@@ -228,7 +251,8 @@ void recurrent_kernel(RecurrentLaunch p) {
   // workgroup on the CU hides the latency instead.
   const int s = tid / kSlot, t = tid % kSlot;
   const int h = g * G + s;
-  const int cq = t % CQ, rg = t / CQ;
+  const int cq = kInWave ? (t / kWave) * CQW + (t % kWave) % CQW : t % CQ;
+  const int rg = kInWave ? (t % kWave) / CQW : t / CQ;
   const gptr<const TS> S_in = to_global(static_cast<const TS *>(p.states[i])) + (size_t)h * D * D;
   typename StateIO<TS>::raw st_raw[RPT];
   auto load_state = [&]() {
@@ -274,13 +298,13 @@ void recurrent_kernel(RecurrentLaunch p) {
     s_b[gr][gs] = p.gates_raw ? strength_from_raw(gb) : gb;
   }
   if (kStoresEveryRow && tid < MAXR) s_dst[tid] = tid < nrows - 1 ? dst_mid : dst_last;
-  if (has_z && tid < G * D) {
+  if (!kPostNorm && has_z && tid < G * D) {
     const float nwv = (float)rnw;
 #pragma unroll
-    for (int r = 0; r < MAXR; ++r)
+    for (int r = 0; r < NZ; ++r)
       if (r < nrows) {
         const float zv = (float)rz[r];
-        s_zw[r][tid] = (p.norm_sigmoid ? __builtin_amdgcn_rcpf(1.0f + __expf(-zv)) : silu(zv)) * nwv;
+        s_zw[kPostNorm ? 0 : r][tid] = norm_gate(zv, p.norm_sigmoid) * nwv;
       }
   }
   __syncthreads();
@@ -323,42 +347,60 @@ void recurrent_kernel(RecurrentLaunch p) {
   for (int r = 0; r < nrows; ++r) {
     const float *qh = &s_qkv[r][0];
     const float *kh = &s_qkv[r][D];
-    float kr[RPT], qr[RPT];  // this thread's rows of k_hat and q_hat
+    // this thread's rows of k_hat (kept for the update) and of q_hat (four at a time)
+    float kr[RPT];
+    float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (RPT % 4 == 0) {  // 16-byte aligned groups of 4 rows
 #pragma unroll
       for (int j = 0; j < RPT; j += 4) {
         *reinterpret_cast<floatx4 *>(&kr[j]) = *reinterpret_cast<const floatx4 *>(&kh[rg * RPT + j]);
-        *reinterpret_cast<floatx4 *>(&qr[j]) = *reinterpret_cast<const floatx4 *>(&qh[rg * RPT + j]);
+        const floatx4 q4 = *reinterpret_cast<const floatx4 *>(&qh[rg * RPT + j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const floatx4 sv = st_reg[j + e];
+          const float kk = kr[j + e], qq = q4[e];
+          pk.x += kk * sv.x; pk.y += kk * sv.y; pk.z += kk * sv.z; pk.w += kk * sv.w;
+          pq.x += qq * sv.x; pq.y += qq * sv.y; pq.z += qq * sv.z; pq.w += qq * sv.w;
+        }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
         kr[j] = kh[rg * RPT + j];
-        qr[j] = qh[rg * RPT + j];
+        const float kk = kr[j], qq = qh[rg * RPT + j];
+        const floatx4 sv = st_reg[j];
+        pk.x += kk * sv.x; pk.y += kk * sv.y; pk.z += kk * sv.z; pk.w += kk * sv.w;
+        pq.x += qq * sv.x; pq.y += qq * sv.y; pq.z += qq * sv.z; pq.w += qq * sv.w;
       }
     }
-    float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-      const float kk = kr[rr], qq = qr[rr];
-      pk.x += kk * st_reg[rr].x; pk.y += kk * st_reg[rr].y; pk.z += kk * st_reg[rr].z; pk.w += kk * st_reg[rr].w;
-      pq.x += qq * st_reg[rr].x; pq.y += qq * st_reg[rr].y; pq.z += qq * st_reg[rr].z; pq.w += qq * st_reg[rr].w;
-    }
-    pk.x = sum_across_groups<CQ>(pk.x); pk.y = sum_across_groups<CQ>(pk.y);
-    pk.z = sum_across_groups<CQ>(pk.z); pk.w = sum_across_groups<CQ>(pk.w);
-    pq.x = sum_across_groups<CQ>(pq.x); pq.y = sum_across_groups<CQ>(pq.y);
-    pq.z = sum_across_groups<CQ>(pq.z); pq.w = sum_across_groups<CQ>(pq.w);
-    if (lane < CQ) {
-      s_red[r & 1][s][wv][cq][0] = pk;
-      s_red[r & 1][s][wv][cq][1] = pq;
-    }
-    __syncthreads();
-    float4 kv = s_red[r & 1][s][0][cq][0], sq = s_red[r & 1][s][0][cq][1];
-#pragma unroll
-    for (int wj = 1; wj < 4; ++wj) {
-      const float4 a0 = s_red[r & 1][s][wj][cq][0], a1 = s_red[r & 1][s][wj][cq][1];
-      kv.x += a0.x; kv.y += a0.y; kv.z += a0.z; kv.w += a0.w;
-      sq.x += a1.x; sq.y += a1.y; sq.z += a1.z; sq.w += a1.w;
+    float4 kv, sq;
+    if constexpr (kInWave) {  // the lanes sharing lane % CQW hold all rows of these columns
+      kv = make_float4(sum_across_groups<CQW>(pk.x), sum_across_groups<CQW>(pk.y), sum_across_groups<CQW>(pk.z),
+                       sum_across_groups<CQW>(pk.w));
+      sq = make_float4(sum_across_groups<CQW>(pq.x), sum_across_groups<CQW>(pq.y), sum_across_groups<CQW>(pq.z),
+                       sum_across_groups<CQW>(pq.w));
+    } else {
+      pk.x = sum_across_groups<CQ>(pk.x); pk.y = sum_across_groups<CQ>(pk.y);
+      pk.z = sum_across_groups<CQ>(pk.z); pk.w = sum_across_groups<CQ>(pk.w);
+      pq.x = sum_across_groups<CQ>(pq.x); pq.y = sum_across_groups<CQ>(pq.y);
+      pq.z = sum_across_groups<CQ>(pq.z); pq.w = sum_across_groups<CQ>(pq.w);
+      if (lane < CQ) {
+        s_red[r & 1][s][wv][cq][0] = pk;
+        s_red[r & 1][s][wv][cq][1] = pq;
+      }
+      __syncthreads();
+      // the four wave partials in pairs, (w0 + w1) + (w2 + w3): the association of
+      // the in-wave butterfly
+      float4 k01 = s_red[r & 1][s][0][cq][0], q01 = s_red[r & 1][s][0][cq][1];
+      float4 k23 = s_red[r & 1][s][2][cq][0], q23 = s_red[r & 1][s][2][cq][1];
+      const float4 k1 = s_red[r & 1][s][1][cq][0], q1 = s_red[r & 1][s][1][cq][1];
+      const float4 k3 = s_red[r & 1][s][3][cq][0], q3 = s_red[r & 1][s][3][cq][1];
+      k01.x += k1.x; k01.y += k1.y; k01.z += k1.z; k01.w += k1.w;
+      q01.x += q1.x; q01.y += q1.y; q01.z += q1.z; q01.w += q1.w;
+      k23.x += k3.x; k23.y += k3.y; k23.z += k3.z; k23.w += k3.w;
+      q23.x += q3.x; q23.y += q3.y; q23.z += q3.z; q23.w += q3.w;
+      kv = make_float4(k01.x + k23.x, k01.y + k23.y, k01.z + k23.z, k01.w + k23.w);
+      sq = make_float4(q01.x + q23.x, q01.y + q23.y, q01.z + q23.z, q01.w + q23.w);
     }
     const float av = s_a[r][s], bv = s_b[r][s];
     const float4 v = *reinterpret_cast<const float4 *>(&s_qkv[r][2 * D + s * D + 4 * cq]);
@@ -366,13 +408,19 @@ void recurrent_kernel(RecurrentLaunch p) {
     u.x = bv * (v.x - av * kv.x); u.y = bv * (v.y - av * kv.y);
     u.z = bv * (v.z - av * kv.z); u.w = bv * (v.w - av * kv.w);
 
-    const bool store_now = kStoresEveryRow || (kStoresLast && r == nrows - 1);
+    // the one-token decode stores its state here; the k-token decode once after
+    // the loop, so that no store in the loop depends on the row
+    const bool store_now = kStoresEveryRow || (MODE == kModeDecode && r == nrows - 1);
     gptr<TS> dst = to_global(kStoresEveryRow ? uniform_ptr(s_dst[r]) : dst_last) + (size_t)h * D * D;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const floatx4 nv = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, kr[rr], u));
       st_reg[rr] = nv;
-      if (store_now) StateIO<TS>::store(dst + (size_t)(rg * RPT + rr) * D + 4 * cq, nv);
+      if (store_now) {
+        StateIO<TS>::store(dst + (size_t)(rg * RPT + rr) * D + 4 * cq, nv);
+        // binary16: issue each narrowed row now rather than holding them all
+        if constexpr (sizeof(TS) == 2 && kStoresEveryRow) __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (MODE == kModeWoa) {  // stash row r0 + r: k_hat of the key head, u and a of the value heads
       gptr<float> srow = to_global(p.stash) + (size_t)(r0 + r) * p.stash_row;
@@ -381,23 +429,70 @@ void recurrent_kernel(RecurrentLaunch p) {
       if (tid < G) srow[stash_a + tid] = s_a[r][tid];
     }
 
-    if (rg == 0) {  // lanes 0..CQ-1 of the slot's first wave hold the head's outputs
+    if (rg == 0) {  // row group 0 holds each column quad's outputs once
       const float qk = s_qk[r];
       float o[4];
       o[0] = p.scale * (av * sq.x + qk * u.x); o[1] = p.scale * (av * sq.y + qk * u.y);
       o[2] = p.scale * (av * sq.z + qk * u.z); o[3] = p.scale * (av * sq.w + qk * u.w);
       const size_t obase = (size_t)(r0 + r) * Hv * D + (size_t)h * D + 4 * cq;
-      if (has_z) {
+      if (kPostNorm && has_z) {  // normalised after the loop
+        *reinterpret_cast<float4 *>(&s_o[kPostNorm ? r : 0][s * D + 4 * cq]) = make_float4(o[0], o[1], o[2], o[3]);
+      } else if (has_z) {
         float ss2 = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
         ss2 = sum_within_span<CQ>(ss2);
         const float inv = rsqrt_hw(ss2 / D + p.norm_eps);
-        const float4 zw = *reinterpret_cast<const float4 *>(&s_zw[r][s * D + 4 * cq]);
+        const float4 zw = *reinterpret_cast<const float4 *>(&s_zw[kPostNorm ? 0 : r][s * D + 4 * cq]);
         o[0] *= inv * zw.x; o[1] *= inv * zw.y; o[2] *= inv * zw.z; o[3] *= inv * zw.w;
       }
-      if (p.geo.out_bf16)
-        store4(static_cast<bf16 *>(p.out) + obase, o);
-      else
-        store4(static_cast<float *>(p.out) + obase, o);
+      if (!(kPostNorm && has_z)) {
+        if (p.geo.out_bf16)
+          store4(static_cast<bf16 *>(p.out) + obase, o);
+        else
+          store4(static_cast<float *>(p.out) + obase, o);
+      }
+    }
+  }
+  if constexpr (MODE == kModeTokens) {
+    const gptr<TS> dst = to_global(dst_last) + (size_t)h * D * D;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) StateIO<TS>::store(dst + (size_t)(rg * RPT + rr) * D + 4 * cq, st_reg[rr]);
+  }
+  if constexpr (kPostNorm) {
+    if (has_z) {  // the gated norm of every (row, value head), one wave each
+      __syncthreads();
+      constexpr int VPL = (D + kWave - 1) / kWave;  // values per lane
+      const int wave = tid / kWave, ln = tid % kWave;
+      const TA *zq = static_cast<const TA *>(p.z), *nw = static_cast<const TA *>(p.norm_w);
+      for (int item = wave; item < nrows * G; item += NT / kWave) {
+        const int r = item / G, s2 = item - r * G;
+        const size_t obase = (size_t)(r0 + r) * Hv * D + (size_t)(g * G + s2) * D;
+        float ov[VPL], zv[VPL], wv[VPL], ss = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int c = min(ln + kWave * j, D - 1);
+          zv[j] = (float)zq[obase + c];
+          wv[j] = (float)nw[c];
+        }
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int c = ln + kWave * j;
+          ov[j] = c < D ? s_o[r][s2 * D + c] : 0.0f;
+          ss += ov[j] * ov[j];
+        }
+        ss = wave_sum(ss);
+        const float inv = rsqrt_hw(ss / D + p.norm_eps);
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) {
+          const int c = ln + kWave * j;
+          if (c < D) {
+            const float v = ov[j] * inv * (norm_gate(zv[j], p.norm_sigmoid) * wv[j]);
+            if (p.geo.out_bf16)
+              st(static_cast<bf16 *>(p.out), obase + c, v);
+            else
+              st(static_cast<float *>(p.out), obase + c, v);
+          }
+        }
+      }
     }
   }
 }
