@@ -21,9 +21,11 @@
 //
 // which equals the token recurrence (U' = T X are the corrected writes u_t).
 //
-// MI355X design.  Three launches:
+// MI355X design.  Three launches (two for a single sequence):
 //   1. chunk_table_kernel: chunk list of the packed batch (chunks restart at each
-//      sequence) and a longest-first sequence order.
+//      sequence; every chunk's entry filled in parallel) and a longest-first
+//      sequence order.  With one sequence the list is implicit (chunk c = rows
+//      64 c ..) and this launch is skipped.
 //   2. prep_kernel, one workgroup per (chunk, value head), all chunks in parallel: K K^T
 //      and Q K^T on bf16 MFMA, the 64x64 UT solve in fp32 (16x16 blocks: the four
 //      diagonal blocks by substitution, the off-diagonal blocks by block products),
@@ -55,9 +57,6 @@ int64_t max_chunks(int n, int64_t T) { return T / kC + n; }
 // ([tile][k-step][lane][8]: one wave-wide 16-byte load is one contiguous 1 KiB
 // block), then Gam[64].
 __host__ __device__ constexpr size_t unit_bytes(int D) { return a256((size_t)4 * D * kC + (size_t)4 * kC * kC + 256); }
-// Per (chunk, key head): K and Q rows in A-fragment order ([row block][k-step][lane][8]),
-// np planes (hi, and lo for fp32 activations).
-__host__ __device__ constexpr size_t kq_bytes(int D, int np) { return a256((size_t)2 * np * kC * D * 2); }
 // Element offset of lane `lane`'s 8 values of fragment (tile, ks) with nks k-steps.
 __host__ __device__ constexpr int frag_off(int tile, int ks, int nks, int lane) { return ((tile * nks + ks) * 64 + lane) * 8; }
 
@@ -67,6 +66,10 @@ struct Tables {
   int32_t *chunk_seq;    // [NC]  sequence of a chunk, -1 for unused slots
   int32_t *chunk_start;  // [NC]  first packed row of a chunk
   int32_t *chunk_len;    // [NC]  rows in a chunk (1..64)
+  // One sequence: no table is built -- its rows are 0 .. T-1 (cu[0] = 0 and
+  // cu[1] = T by contract), so chunk c starts at row 64 c.
+  int implicit;
+  int T;
 };
 
 size_t tables_bytes(int n, int64_t NC) {
@@ -74,7 +77,7 @@ size_t tables_bytes(int n, int64_t NC) {
 }
 
 Tables carve_tables(char *ws, int n, int64_t NC) {
-  Tables t;
+  Tables t{};
   size_t off = 0;
   t.seq_chunk0 = reinterpret_cast<int32_t *>(ws + off); off += a256(4 * (size_t)(n + 1));
   t.order = reinterpret_cast<int32_t *>(ws + off); off += a256(4 * (size_t)n);
@@ -162,14 +165,21 @@ __global__ __launch_bounds__(256) void chunk_table_kernel(const int32_t *cu, int
   if (tid == 0) tb.seq_chunk0[n] = total;
   for (int s = s0; s < s1; ++s) {
     tb.seq_chunk0[s] = run;
-    const int len = cu[s + 1] - cu[s];
-    const int nc = (len + kC - 1) / kC;
-    for (int c = 0; c < nc; ++c) {
-      tb.chunk_seq[run + c] = s;
-      tb.chunk_start[run + c] = cu[s] + kC * c;
-      tb.chunk_len[run + c] = min(kC, len - kC * c);
+    run += (cu[s + 1] - cu[s] + kC - 1) / kC;
+  }
+  __syncthreads();  // seq_chunk0 complete (workgroup-scope ordering of the global writes)
+  // every chunk in parallel: its sequence is the last s with seq_chunk0[s] <= chunk
+  for (int idx = tid; idx < total; idx += 256) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (tb.seq_chunk0[mid] <= idx) lo = mid; else hi = mid - 1;
     }
-    run += nc;
+    const int c = idx - tb.seq_chunk0[lo];
+    const int len = cu[lo + 1] - cu[lo];
+    tb.chunk_seq[idx] = lo;
+    tb.chunk_start[idx] = cu[lo] + kC * c;
+    tb.chunk_len[idx] = min(kC, len - kC * c);
   }
   for (int64_t idx = total + tid; idx < NC; idx += 256) tb.chunk_seq[idx] = -1;
   // longest sequences first (rank sort; identity order for very large batches)
@@ -226,9 +236,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   constexpr int NIG = D / 8 / 4;  // groups of 8 K columns staged per wave
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   const int cidx = blockIdx.x / Hv, h = blockIdx.x - cidx * Hv;
-  const int seq = tb.chunk_seq[cidx];
+  const int seq = tb.implicit ? (cidx * kC < tb.T ? 0 : -1) : tb.chunk_seq[cidx];
   if (seq < 0) return;
-  const int t0 = tb.chunk_start[cidx], L = tb.chunk_len[cidx];
+  const int t0 = tb.implicit ? cidx * kC : tb.chunk_start[cidx];
+  const int L = tb.implicit ? min(kC, tb.T - t0) : tb.chunk_len[cidx];
   const int g = h / G;
   const int tid = threadIdx.x, lane = tid % kWave, lr = lane % 16, lg = lane / 16;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -572,8 +583,9 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     b = (b - r) + (r % 8) * NCB + r / 8;
   }
   const int cb = b % NCB, hq = b / NCB, h = hq % Hv, q = hq / Hv;
-  const int seq = tb.order[q];
-  const int c_first = tb.seq_chunk0[seq], nch = tb.seq_chunk0[seq + 1] - c_first;
+  const int seq = tb.implicit ? 0 : tb.order[q];
+  const int c_first = tb.implicit ? 0 : tb.seq_chunk0[seq];
+  const int nch = tb.implicit ? (tb.T + kC - 1) / kC : tb.seq_chunk0[seq + 1] - c_first;
   if (nch == 0) return;  // zero-length sequence: state unchanged
   // chunk c of the sequence starts at row seq_t0 + 64 c (no table loads in the loop)
   const int seq_t0 = p.cu[seq], seq_len = p.cu[seq + 1] - seq_t0;
@@ -849,10 +861,15 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
   const int64_t NC = max_chunks(p.n, p.T);
   char *ws = static_cast<char *>(p.workspace);
   Tables tb = carve_tables(ws, p.n, NC);
+  tb.implicit = p.n == 1;
+  tb.T = (int)p.T;
   char *units = ws + a256(tables_bytes(p.n, NC));
-  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, stream, p.cu, p.n, NC, tb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!tb.implicit) {
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, stream, p.cu, p.n, NC, tb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hv)), dim3(256), 0, stream, p, tb, units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
