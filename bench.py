@@ -28,6 +28,7 @@ import numpy as np
 
 HBM_PEAK = 8.0e12           # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15     # FLOP/s, MI355X dense bf16
+VALU_FP32_PEAK = 157.3e12   # FLOP/s, MI355X fp32 vector (packed issue; half without it)
 
 D, HK, HV, C = 128, 16, 32, 64
 STATE_BYTES = HV * D * D * 4            # one sequence's fp32 state, 2 MiB
@@ -45,9 +46,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "48f5024d51d4ab2e6baf069aa7a551448f0b37ae6ce7e491ffdba8c2e8c3cfcc",
-    "fetch_kib": 136030.8, "write_kib": 269312.0,
-    "fetch_scale": 1048576.0 / 524302.0, "write_scale": 1048576.0 / 1048576.0,
+    "sha256": "ebd8cec03d5b0931803c6be59afb618249998d55a32971e02a43f65b774e7fde",
+    "fetch_kib": 136037.7, "write_kib": 269312.0,
+    "fetch_scale": 1048576.0 / 524302.2, "write_scale": 1048576.0 / 1048576.0,
 }
 
 
@@ -263,17 +264,23 @@ def variant_phases(torch, B, W, w, reps=10):
     fold = lambda: B.gdn_fold_accepted(w.v_x, rp, hp, stash, w.v_cu, w.v_nacc, dims)
     ms_v, ms_f = _timed(torch, woa, reps), _timed(torch, fold, reps)
     vb, fb = woa_verify_bytes(w.v_ks), fold_bytes(v["n_acc"])
+    # fp32 arithmetic per row and value head: S k and S q (2 d^2 each), S <- a S + u k^T (3 d^2)
+    row_flops = 7 * D * D * HV * w.v_rows
+    valu = lambda ms: {"bound": "alu", "tflops": row_flops / (ms / 1e3) / 1e12,
+                       "frac": row_flops / (ms / 1e3) / VALU_FP32_PEAK,
+                       "frac_unpacked": row_flops / (ms / 1e3) / (VALU_FP32_PEAK / 2)}
     res["verify_woa"] = {"rows": w.v_rows, "ms": ms_v, "fold_ms": ms_f, "tokens_per_s": w.v_rows / (ms_v / 1e3),
                          "gb_per_s": vb / (ms_v / 1e3) / 1e9, "hbm_frac": vb / (ms_v / 1e3) / HBM_PEAK,
                          "fold_gb_per_s": fb / (ms_f / 1e3) / 1e9, "fold_hbm_frac": fb / (ms_f / 1e3) / HBM_PEAK,
-                         "bytes": vb, "fold_bytes": fb}
+                         "bytes": vb, "fold_bytes": fb, "valu": valu(ms_v)}
     # k consecutive tokens per sequence on the verify's rows (state written once)
     toks = lambda: B.gdn_decode_tokens(w.v_x, w.v_w, rp, w.v_a, w.v_b, hp, w.v_cu, w.v_maxk, w.v_out, dims,
                                        z=w.v_z, norm_w=w.v_nw)
     ms_t = _timed(torch, toks, reps)
     tb = tokens_bytes(w.v_ks)
     res["decode_tokens"] = {"rows": w.v_rows, "ms": ms_t, "tokens_per_s": w.v_rows / (ms_t / 1e3),
-                            "gb_per_s": tb / (ms_t / 1e3) / 1e9, "hbm_frac": tb / (ms_t / 1e3) / HBM_PEAK}
+                            "gb_per_s": tb / (ms_t / 1e3) / 1e9, "hbm_frac": tb / (ms_t / 1e3) / HBM_PEAK,
+                            "valu": valu(ms_t)}
     del h, stash
     # binary16 states: the decode workload, 100 steps
     d = W.config(2)
