@@ -17,10 +17,13 @@
 namespace gdn {
 namespace {
 
-// Packed rows per workgroup: every row load of a thread is issued at once (kept
-// raw until used), so a 256-thread workgroup has 128 KiB (bf16 input) in flight.
+// Packed rows per thread: every row load of a thread is issued at once (kept raw
+// until used).  Short blocks (8 rows plus 3 history rows, re-read from L2 by the
+// neighbouring block) and up to four waves per SIMD let the loads, the arithmetic
+// and the stores of different workgroups overlap; measured faster than 16 or 32
+// rows per thread at two waves per SIMD.
 template <typename TA>
-constexpr int conv_rows() { return sizeof(TA) == 2 ? 32 : 16; }
+constexpr int conv_rows() { return 8; }
 
 // Eight consecutive channels of one row, widened to fp32.
 __device__ __forceinline__ void load8(const bf16 *p, float v[8]) {
@@ -73,7 +76,7 @@ struct Raw8<float> {
 // workgroup); a q or k head (d channels) is d/8 consecutive lanes, which reduce
 // its squared norm with shuffles.
 template <int D, int K, typename TA, typename TY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void conv_l2norm_kernel(ConvLaunch p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void conv_l2norm_kernel(ConvLaunch p) {
   constexpr int TPH = D / 8;  // lanes per head
   constexpr int R = conv_rows<TA>();
   const int C = p.geo.conv_dim, Hk = p.geo.Hk;
