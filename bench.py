@@ -413,7 +413,25 @@ def cpu_baseline(W):
     t_ver = (time.perf_counter() - t0) * (int(v["cu"][-1]) / len(rows))
     t_total = t_pre + t_dec + t_ver
     tokens = 4096 + 128 * 100 + int(v["cu"][-1])
+    # the same oracle on one thread, decode of 8 sequences for 2 steps (per sequence-token)
+    oracle.set_num_threads(1)
+    S1, ring1 = d["S0"][:8], d["ring"][:8]
+    t0 = time.perf_counter()
+    for s in range(2):
+        r = oracle.decode(d["x"][s][:8], d["conv_w"], ring1, d["a"][s][:8], d["b"][s][:8], S1, dims.Hk, dims.Hv,
+                          dims.dk, dims.dv, z=d["z"][s][:8], norm_w=d["norm_w"])
+        S1, ring1 = r["S"], r["ring"]
+    one_thread = 16 / (time.perf_counter() - t0)
+    oracle.set_num_threads(threads)
+    host = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            host = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": tokens / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpu": host, "decode_tokens_per_s_all_threads": 48 * 10 / (t_dec * (48 / 128) * (10 / 100)),
+            "decode_tokens_per_s_one_thread": one_thread,
             "sample": "fp64 oracle (C, OpenMP over sequence x value head) on: prefill of the first 1024 of "
                       "4096 tokens (all 32 heads, conv front and gated norm), decode of 48 of 128 sequences "
                       "for 10 of 100 steps, verify + commit of 24 of 64 sequences; each phase's time scaled "
