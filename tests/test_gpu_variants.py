@@ -284,7 +284,7 @@ def test_raw_gates_and_sigmoid_norm_prefill():
 # several consecutive tokens per sequence
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state", "n128"])
+@pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state", "n128", "config3_rows"])
 def test_decode_tokens(case):
     """k_i tokens per sequence (1..17) against the oracle's token-by-token decode;
     the final state equals, bit for bit, the last state the verify stores for the
@@ -299,9 +299,12 @@ def test_decode_tokens(case):
         ks = [12, 7, 1, 16]
         d = W.verify_inputs(3110, len(ks), W.QWEN_DIMS, ks=ks)
         d["S0"] = f16_exact(d["S0"])
-    else:  # the widest batch, k = 1 and 17 alternating, d = 64 heads
+    elif case == "n128":  # the widest batch, k = 1 and 17 alternating, d = 64 heads
         ks = [1, 17] * 64
         d = W.verify_inputs(3113, len(ks), W.Dims(Hk=4, Hv=8, dk=64, dv=64, K=4), ks=ks)
+    else:  # the launch the bench times: every row of the 64-sequence verify workload
+        d = W.config(3)
+        ks = list(d["ks"])
     state = "f16" if case == "f16_state" else "f32"
     sdt = torch.float16 if state == "f16" else torch.float32
     dims, act = d["dims"], act_dtype(d)
