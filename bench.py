@@ -264,7 +264,9 @@ def variant_phases(torch, B, W, w, reps=10):
     fold = lambda: B.gdn_fold_accepted(w.v_x, rp, hp, stash, w.v_cu, w.v_nacc, dims)
     ms_v, ms_f = _timed(torch, woa, reps), _timed(torch, fold, reps)
     vb, fb = woa_verify_bytes(w.v_ks), fold_bytes(v["n_acc"])
-    # fp32 arithmetic per row and value head: S k and S q (2 d^2 each), S <- a S + u k^T (3 d^2)
+    # k-token decode, row by row in fp32: S k and S q (2 d^2 each), S <- a S + u k^T (3 d^2)
+    # per row and value head (the write-on-accept verify takes the WY form on the matrix
+    # cores and is bound by its bytes)
     row_flops = 7 * D * D * HV * w.v_rows
     valu = lambda ms: {"bound": "alu", "tflops": row_flops / (ms / 1e3) / 1e12,
                        "frac": row_flops / (ms / 1e3) / VALU_FP32_PEAK,
@@ -272,7 +274,7 @@ def variant_phases(torch, B, W, w, reps=10):
     res["verify_woa"] = {"rows": w.v_rows, "ms": ms_v, "fold_ms": ms_f, "tokens_per_s": w.v_rows / (ms_v / 1e3),
                          "gb_per_s": vb / (ms_v / 1e3) / 1e9, "hbm_frac": vb / (ms_v / 1e3) / HBM_PEAK,
                          "fold_gb_per_s": fb / (ms_f / 1e3) / 1e9, "fold_hbm_frac": fb / (ms_f / 1e3) / HBM_PEAK,
-                         "bytes": vb, "fold_bytes": fb, "valu": valu(ms_v)}
+                         "bytes": vb, "fold_bytes": fb, "bound": "hbm"}
     # k consecutive tokens per sequence on the verify's rows (state written once)
     toks = lambda: B.gdn_decode_tokens(w.v_x, w.v_w, rp, w.v_a, w.v_b, hp, w.v_cu, w.v_maxk, w.v_out, dims,
                                        z=w.v_z, norm_w=w.v_nw)

@@ -133,7 +133,6 @@ void recurrent_kernel(RecurrentLaunch p) {
   constexpr int NCH = (2 + G) * D;     // q, k, and G v heads
   constexpr int NT = kSlot * G;
   constexpr bool kStoresEveryRow = MODE == kModeVerify;
-  constexpr bool kStoresLast = MODE == kModeDecode || MODE == kModeTokens;
   constexpr bool kAdvancesRing = MODE == kModeDecode || MODE == kModeTokens;
   // Write-on-accept verify and k-token decode: a wave holds every row group of its
   // CQW column quads, so the per-row reductions are shuffles within the wave and
@@ -502,8 +501,13 @@ void recurrent_kernel(RecurrentLaunch p) {
 template <int D, int G, int MAXR, int MODE, typename TA>
 hipError_t launch_rec_ts(const RecurrentLaunch &p, hipStream_t stream) {
   const dim3 grid(p.n * p.geo.Hk), block(kSlot * G);
+  // the write-on-accept verify over fp32 states at d >= 64 takes the WY form
+  // (recurrent_wy.h); this kernel serves it with binary16 states and at d = 32.
+  constexpr bool kF32ViaWy = MODE == kModeWoa && D >= 64;
   if (p.state_f16)
     hipLaunchKernelGGL((recurrent_kernel<D, G, MAXR, MODE, TA, _Float16>), grid, block, 0, stream, p);
+  else if constexpr (kF32ViaWy)
+    return hipErrorInvalidValue;
   else
     hipLaunchKernelGGL((recurrent_kernel<D, G, MAXR, MODE, TA, float>), grid, block, 0, stream, p);
   return hipGetLastError();

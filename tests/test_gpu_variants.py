@@ -43,16 +43,26 @@ def _stash_parts(stash, T, dims):
             s[:, Hk * d + Hv * d: Hk * d + Hv * d + Hv])
 
 
+def _wy_form(dims, state):
+    """fp32 states at d >= 64: the write-on-accept verify takes the WY form on the
+    matrix cores instead of the row-by-row recurrence."""
+    return state == "f32" and dims.dk >= 64
+
+
 # ---------------------------------------------------------------------------
 # write-on-accept verify and fold
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("case,state", [("config3", "f32"), ("config3", "f16"), ("tiny_fp32", "f32"),
-                                        ("edge_k", "f32"), ("n128_k1", "f32"), ("d64_g4", "f16")])
+                                        ("edge_k", "f32"), ("n128_k1", "f32"), ("d64_g4", "f16"),
+                                        ("d64_g4", "f32"), ("extreme_raw_gates", "f32")])
 def test_woa_verify_and_fold(case, state):
     """Outputs and stash against the oracle; the fold of the accepted rows against
-    the oracle, and bit for bit against the state the write-all verify records
-    after the same row; the conv state against the oracle's commit."""
+    the oracle and against the state the write-all verify records after the same
+    row (bit for bit where both take the rows one by one: binary16 states and
+    d = 32; fp32 states at d >= 64 take the WY form, whose sums associate
+    differently); the conv state against the oracle's commit."""
+    gates = "direct"
     if case == "config3":
         d = W.config(3)
         sample = np.array([0, 5, 19, 40, 63])
@@ -67,6 +77,13 @@ def test_woa_verify_and_fold(case, state):
         ks = np.array(([1, 16, 5, 1] * 32)[:128])
         d = W.verify_inputs(3111, 128, W.QWEN_DIMS, ks=ks)
         sample = np.array([0, 1, 2, 3, 64, 126, 127])
+    elif case == "extreme_raw_gates":  # raw g, beta at +-30: products of decays underflow, b saturates
+        d = W.verify_inputs(3117, 6, W.QWEN_DIMS, ks=[16, 9, 2, 13, 16, 5])
+        rng = np.random.default_rng(3117)
+        d["a"] = rng.choice([-30.0, -3.0, 0.0, 3.0, 30.0], size=d["a"].shape).astype(np.float32)
+        d["b"] = rng.choice([-30.0, 0.0, 30.0], size=d["b"].shape).astype(np.float32)
+        gates = "raw"
+        sample = np.arange(6)
     else:  # d = 64, four value heads per key head
         d = W.verify_inputs(3112, 7, W.Dims(Hk=2, Hv=8, dk=64, dv=64, K=4), act="bf16")
         sample = np.arange(7)
@@ -77,7 +94,7 @@ def test_woa_verify_and_fold(case, state):
     dims, act = d["dims"], act_dtype(d)
     cu, ks, n_acc = d["cu"], d["ks"], d["n_acc"]
     T = int(cu[-1])
-    opt = B.options(sdt)
+    opt = B.options(sdt, gates=gates)
     x, w = tdev(d["x"], act), tdev(d["conv_w"], act)
     a, b = tdev(d["a"], torch.float32), tdev(d["b"], torch.float32)
     z, nw = tdev(d["z"], act), tdev(d["norm_w"], act)
@@ -96,27 +113,39 @@ def test_woa_verify_and_fold(case, state):
     rows, cu_s = _sample_rows(cu, sample)
     ref = oracle.verify_woa(d["x"][rows], d["conv_w"], d["ring"][sample], d["a"][rows], d["b"][rows],
                             d["S0"][sample], cu_s, dims.Hk, dims.Hv, dims.dk, dims.dv, z=d["z"][rows],
-                            norm_w=d["norm_w"], state=state)
+                            norm_w=d["norm_w"], state=state, gates=gates)
     g = host(out)[rows].reshape(len(rows), dims.Hv, dims.dv)
     assert slice_err(g, ref["out"], row_seq_of(cu_s)) < TOL_OUT
     sk, su, sa = _stash_parts(stash, T, dims)
     assert slice_err(sk[rows], ref["stash_k"], row_seq_of(cu_s)) < 1e-5
     assert slice_err(su[rows], ref["stash_u"], row_seq_of(cu_s)) < TOL_STATE
-    assert np.array_equal(sa[rows], d["a"][rows].astype(np.float64))
+    if gates == "raw":  # the decays the kernel derived from g (hardware exp and reciprocal)
+        assert np.allclose(sa[rows], ref["stash_a"], rtol=1e-5, atol=0.0)
+    else:
+        assert np.array_equal(sa[rows], d["a"][rows].astype(np.float64))
 
     # the write-all verify on the same inputs, for the bitwise comparison
     ds2 = DeviceStates(d["S0"], d["ring"], act, sdt)
     inter, tab = _tables(ds2, ks, dims, sdt)
     out2 = torch.empty_like(out)
     B.gdn_verify_multi(x, w, ds2.ring_ptrs, a, b, tab, cu_t, max_k, out2, dims, z=z, norm_w=nw, opt=opt)
-    assert torch.equal(out, out2)
+    wy = _wy_form(dims, state)
+    if wy:
+        assert slice_err(host(out).reshape(T, dims.Hv, dims.dv), host(out2).reshape(T, dims.Hv, dims.dv),
+                         row_seq_of(cu)) < TOL_OUT
+    else:
+        assert torch.equal(out, out2)
 
-    B.gdn_fold_accepted(x, ds.ring_ptrs, ds.h_ptrs, stash, cu_t, torch.from_numpy(n_acc).to(DEV), dims, opt=opt)
+    B.gdn_fold_accepted(x, ds.ring_ptrs, ds.h_ptrs, stash, cu_t, torch.from_numpy(n_acc).to(DEV), dims,
+                        opt=B.options(sdt))  # (the stash holds the decays themselves)
     torch.cuda.synchronize()
     for i in range(d["n"]):
         na = int(n_acc[i])
         recorded = inter[i][na - 1] if na < ks[i] else ds2.h[i]
-        assert torch.equal(ds.h[i], recorded), (i, na, int(ks[i]))
+        if wy:
+            assert slice_err(host(ds.h[i])[None], host(recorded)[None]) < TOL_STATE, (i, na, int(ks[i]))
+        else:
+            assert torch.equal(ds.h[i], recorded), (i, na, int(ks[i]))
     S_ref, ring_ref = oracle.fold_accepted(d["S0"][sample], ref["stash_k"], ref["stash_u"], ref["stash_a"], cu_s,
                                            n_acc[sample], d["ring"][sample], d["x"][rows], state=state)
     assert slice_err(ds.h_host()[sample], S_ref) < tol_s
@@ -284,11 +313,13 @@ def test_raw_gates_and_sigmoid_norm_prefill():
 # several consecutive tokens per sequence
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state", "n128", "config3_rows"])
+@pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state", "n128", "config3_rows",
+                                  "extreme_raw_gates"])
 def test_decode_tokens(case):
     """k_i tokens per sequence (1..17) against the oracle's token-by-token decode;
     the final state equals, bit for bit, the last state the verify stores for the
     same rows (k_i <= 16), and the conv state advances over all the rows."""
+    gates = "direct"
     if case == "mixed_bf16":
         ks = [17, 1, 5, 16, 2, 9, 17, 3]
         d = W.verify_inputs(3108, len(ks), W.QWEN_DIMS, ks=ks)
@@ -302,6 +333,13 @@ def test_decode_tokens(case):
     elif case == "n128":  # the widest batch, k = 1 and 17 alternating, d = 64 heads
         ks = [1, 17] * 64
         d = W.verify_inputs(3113, len(ks), W.Dims(Hk=4, Hv=8, dk=64, dv=64, K=4), ks=ks)
+    elif case == "extreme_raw_gates":  # raw g, beta at +-30: products of decays underflow, b saturates
+        ks = [17, 16, 9, 2, 1, 13]
+        d = W.verify_inputs(3116, len(ks), W.QWEN_DIMS, ks=ks)
+        rng = np.random.default_rng(3116)
+        d["a"] = rng.choice([-30.0, -3.0, 0.0, 3.0, 30.0], size=d["a"].shape).astype(np.float32)
+        d["b"] = rng.choice([-30.0, 0.0, 30.0], size=d["b"].shape).astype(np.float32)
+        gates = "raw"
     else:  # the launch the bench times: every row of the 64-sequence verify workload
         d = W.config(3)
         ks = list(d["ks"])
@@ -310,7 +348,7 @@ def test_decode_tokens(case):
     dims, act = d["dims"], act_dtype(d)
     cu = d["cu"]
     T = int(cu[-1])
-    opt = B.options(sdt)
+    opt = B.options(sdt, gates=gates)
     ds = DeviceStates(d["S0"], d["ring"], act, sdt)
     out = torch.empty((T, dims.Hv * dims.dv), dtype=torch.float32, device=DEV)
     x, w = tdev(d["x"], act), tdev(d["conv_w"], act)
@@ -319,7 +357,7 @@ def test_decode_tokens(case):
     B.gdn_decode_tokens(x, w, ds.ring_ptrs, a, b, ds.h_ptrs, tdev(cu, torch.int32), int(max(ks)), out, dims,
                         z=z, norm_w=nw, opt=opt)
     r = oracle.decode_tokens(d["x"], d["conv_w"], d["ring"], d["a"], d["b"], d["S0"], cu, dims.Hk, dims.Hv,
-                             dims.dk, dims.dv, z=d["z"], norm_w=d["norm_w"], state=state)
+                             dims.dk, dims.dv, z=d["z"], norm_w=d["norm_w"], state=state, gates=gates)
     assert slice_err(host(out).reshape(T, dims.Hv, dims.dv), r["out"], row_seq_of(cu)) < TOL_OUT
     assert slice_err(ds.h_host(), r["S"]) < (TOL_STATE_F16 if state == "f16" else TOL_STATE)
     assert np.array_equal(ds.ring_host(), r["ring"])
