@@ -46,9 +46,9 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "ebd8cec03d5b0931803c6be59afb618249998d55a32971e02a43f65b774e7fde",
-    "fetch_kib": 136037.7, "write_kib": 269312.0,
-    "fetch_scale": 1048576.0 / 524302.2, "write_scale": 1048576.0 / 1048576.0,
+    "sha256": "4d405e9cb102b973fafbe3ce17455974c2db08b90ecf6ed1b4353952276c8482",
+    "fetch_kib": 136039.3, "write_kib": 269312.0,
+    "fetch_scale": 1048576.0 / 524302.0, "write_scale": 1048576.0 / 1048576.0,
 }
 
 
