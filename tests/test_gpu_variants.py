@@ -55,7 +55,8 @@ def _wy_form(dims, state):
 
 @pytest.mark.parametrize("case,state", [("config3", "f32"), ("config3", "f16"), ("tiny_fp32", "f32"),
                                         ("edge_k", "f32"), ("n128_k1", "f32"), ("d64_g4", "f16"),
-                                        ("d64_g4", "f32"), ("extreme_raw_gates", "f32")])
+                                        ("d64_g4", "f32"), ("extreme_raw_gates", "f32"), ("g1_f32act", "f32"),
+                                        ("g4_d128_k3", "f32")])
 def test_woa_verify_and_fold(case, state):
     """Outputs and stash against the oracle; the fold of the accepted rows against
     the oracle and against the state the write-all verify records after the same
@@ -84,6 +85,12 @@ def test_woa_verify_and_fold(case, state):
         d["b"] = rng.choice([-30.0, 0.0, 30.0], size=d["b"].shape).astype(np.float32)
         gates = "raw"
         sample = np.arange(6)
+    elif case == "g1_f32act":  # one value head per key head, fp32 activations
+        d = W.verify_inputs(3118, 5, W.Dims(Hk=4, Hv=4, dk=128, dv=128, K=4), act="f32", ks=[16, 3, 11, 1, 8])
+        sample = np.arange(5)
+    elif case == "g4_d128_k3":  # four value heads per key head at d = 128, a 3-tap conv
+        d = W.verify_inputs(3119, 5, W.Dims(Hk=2, Hv=8, dk=128, dv=128, K=3), act="bf16", ks=[7, 16, 2, 12, 5])
+        sample = np.arange(5)
     else:  # d = 64, four value heads per key head
         d = W.verify_inputs(3112, 7, W.Dims(Hk=2, Hv=8, dk=64, dv=64, K=4), act="bf16")
         sample = np.arange(7)
