@@ -352,6 +352,24 @@ def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+def gemm_tflops(torch, n=8192, reps=5):
+    """Attainable dense bf16 matrix-core rate: a plain n x n x n product through
+    torch (the vendor GEMM library), TFLOP/s."""
+    a = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((n, n), dtype=torch.bfloat16, device="cuda")
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms / 1e3) / 1e12
+
+
 def fill_bandwidth(torch, nbytes=1 << 30, reps=5):
     """Attainable write-only bandwidth of a plain device fill (torch), GB/s."""
     dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -531,8 +549,10 @@ def main():
         "phases": phases,
         "variants": variant_phases(torch, B, W, w),
         "attainable": {"copy_gb_per_s": copy_bandwidth(torch), "fill_gb_per_s": fill_bandwidth(torch),
-                       "note": "plain 1 GiB device-to-device copy (read + write bytes / time) and 1 GiB fill "
-                               "(bytes written / time)"},
+                       "bf16_gemm_tflops": gemm_tflops(torch),
+                       "note": "plain 1 GiB device-to-device copy (read + write bytes / time), 1 GiB fill "
+                               "(bytes written / time), and an 8192^3 bf16 product through torch.mm "
+                               "(2 n^3 / time)"},
         "wall_s_timed": t_wall,
     }
     if not args.no_cpu_baseline:
