@@ -344,7 +344,10 @@ gdn_status gdn_verify_commit(const gdn_commit_args *args, void *stream);
  *   woa_stash binding (layer_struct.rs), gdn_woa_stash_seq_floats, gdn_woa_bind
  *   and gdn_fold_accepted (trait_layer.rs).  The pages name the stash, not its
  *   contents; the (k_hat, u, a) rows are the plainest contents that let the fold
- *   reproduce the recorded states exactly.
+ *   reproduce the recorded states.  fp32 states at d_k = d_v = 64 or 128 are
+ *   verified in the WY form over the k_i rows (outputs and u within fp32 rounding
+ *   of the row-by-row values); binary16 states and d = 32 row by row, whose fold
+ *   reproduces gdn_verify_multi's states bit for bit.
  * ------------------------------------------------------------------------- */
 typedef struct gdn_woa_args {
   uint32_t struct_size;        /* sizeof(gdn_woa_args)                          */
@@ -388,8 +391,10 @@ gdn_status gdn_verify_woa(const gdn_woa_args *args, void *stream);
  *   order, every value head's state becomes a_r S + u_r k_r^T (rounded after every
  *   row when the state is binary16), reading stash row r; the state is read and
  *   written once.  The conv state becomes the last K-1 rows of
- *   [old conv state ; rows 0..n_i-1].  The result equals the state
- *   gdn_verify_multi records after row n_i - 1.
+ *   [old conv state ; rows 0..n_i-1].  The result is the state
+ *   gdn_verify_multi records after row n_i - 1 (bit for bit when the stash comes
+ *   from a row-by-row verify, within fp32 rounding when it comes from the WY form;
+ *   see gdn_verify_woa).
  *   Defined by: gdn_fold_accepted (trait_layer.rs), gdn_wy4_fold_k (layer_struct.rs).
  * ------------------------------------------------------------------------- */
 typedef struct gdn_fold_args {

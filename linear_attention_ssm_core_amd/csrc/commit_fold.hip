@@ -64,8 +64,9 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4)
 }
 
 // Fold: blockIdx.y < H_v is one value head's state, read once, advanced over the
-// accepted rows from the stash in order (the verify's rank-1 update, bit for bit),
-// and written once; the other blocks advance the conv state.  Thread t holds
+// accepted rows from the stash in order (the verify's rank-1 update, in the same
+// operation order), and written once; the other blocks advance the conv state.
+// Thread t holds
 // column quad t % (D/4) of the D^2/1024 consecutive rows from (t / (D/4)) D^2/1024,
 // as in the verify.
 template <int D, typename TE, typename TS>

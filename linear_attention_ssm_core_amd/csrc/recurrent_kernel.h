@@ -71,8 +71,8 @@ struct StateIO<_Float16> {
 };
 
 // S <- a S + u k^T on one row of 4 columns: the same operation order in every
-// kernel that advances a state, so that a fold of stashed rows reproduces the
-// verify's recorded states bit for bit.
+// kernel that advances a state, so that a fold of rows stashed by this kernel
+// reproduces the verify's recorded states bit for bit.
 __device__ __forceinline__ floatx4 rank1_update(floatx4 s, float a, float k, floatx4 u) {
   floatx4 r;
   r.x = __builtin_fmaf(k, u.x, a * s.x);
@@ -146,7 +146,9 @@ void recurrent_kernel(RecurrentLaunch p) {
   // value head), the same code for both layouts; together with reductions of the
   // same association (a butterfly over row groups in the in-wave layout, pairs of
   // wave partials in the other) every multi-row mode produces bit-identical
-  // outputs and update vectors, so a fold of the stash equals the recorded states.
+  // outputs and update vectors, so a fold of the stash equals the recorded states
+  // (the write-on-accept verify runs here for binary16 states and d = 32; fp32
+  // states at d >= 64 take the WY form of recurrent_wy.h).
   constexpr bool kPostNorm = MODE != kModeDecode;
   static_assert(RPT * RG == D, "head dim must split over the row groups");
   static_assert((MODE == kModeDecode) == (MAXR == 1), "one-token decode is the MAXR = 1 instance");
