@@ -46,7 +46,7 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "4d405e9cb102b973fafbe3ce17455974c2db08b90ecf6ed1b4353952276c8482",
+    "sha256": "4268cd16915aa61e829dd975d27d51fa96da7cd3e03e560fdd0bf50495c19f0f",
     "fetch_kib": 136039.3, "write_kib": 269312.0,
     "fetch_scale": 1048576.0 / 524302.0, "write_scale": 1048576.0 / 1048576.0,
 }
