@@ -321,7 +321,7 @@ def test_raw_gates_and_sigmoid_norm_prefill():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("case", ["mixed_bf16", "k17_tiny_fp32", "f16_state", "n128", "config3_rows",
-                                  "extreme_raw_gates"])
+                                  "extreme_raw_gates", "zero_decays"])
 def test_decode_tokens(case):
     """k_i tokens per sequence (1..17) against the oracle's token-by-token decode;
     the final state equals, bit for bit, the last state the verify stores for the
@@ -347,6 +347,12 @@ def test_decode_tokens(case):
         d["a"] = rng.choice([-30.0, -3.0, 0.0, 3.0, 30.0], size=d["a"].shape).astype(np.float32)
         d["b"] = rng.choice([-30.0, 0.0, 30.0], size=d["b"].shape).astype(np.float32)
         gates = "raw"
+    elif case == "zero_decays":  # a = 0 (the past forgotten) and a = 1 among ordinary decays
+        ks = [5, 17, 3, 16]
+        d = W.verify_inputs(3120, len(ks), W.QWEN_DIMS, ks=ks)
+        rng = np.random.default_rng(3120)
+        pick = rng.random(d["a"].shape)
+        d["a"] = np.where(pick < 0.15, 0.0, np.where(pick > 0.85, 1.0, d["a"])).astype(np.float32)
     else:  # the launch the bench times: every row of the 64-sequence verify workload
         d = W.config(3)
         ks = list(d["ks"])
