@@ -35,8 +35,8 @@
 //   3. spine_kernel, one workgroup per (sequence, value head, 32-column block of d_v):
 //      the serial pass over the chunks with specialised waves (K rows, Q rows, state
 //      owners); see the comment at the kernel.  Columns of h evolve independently, so a
-//      128-wide state splits into 4 workgroups, mapped onto one XCD so they share the
-//      head's operands through one L2.
+//      128-wide state splits into 4 workgroups; those of the value heads of one key
+//      head are mapped onto one XCD so they share its operands through one L2.
 // Precision: fp32-derived operands (h, X, T, E, MT, and fp32 activations) enter
 // MFMA as bf16 hi + lo; a product takes hi*hi + hi*lo + lo*hi, about 2^-16
 // relative, which keeps states within 1e-4 of the fp64 recurrence.
@@ -235,7 +235,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   constexpr int NTI = D / 16;
   constexpr int NIG = D / 8 / 4;  // groups of 8 K columns staged per wave
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
-  const int cidx = blockIdx.x / Hv, h = blockIdx.x - cidx * Hv;
+  // Workgroups go round-robin over the 8 XCDs; within each group of 8 * G, remap so
+  // that the G value heads of a key head (which read the same K and Q rows) run on
+  // one XCD and share them through its L2.
+  int b = blockIdx.x;
+  {
+    const int nb = gridDim.x, grp = 8 * G;
+    if (b < nb - nb % grp) {
+      const int r = b % grp;
+      b = (b - r) + (r % 8) * G + r / 8;
+    }
+  }
+  const int cidx = b / Hv, h = b - cidx * Hv;
   const int seq = tb.implicit ? (cidx * kC < tb.T ? 0 : -1) : tb.chunk_seq[cidx];
   if (seq < 0) return;
   const int t0 = tb.implicit ? cidx * kC : tb.chunk_start[cidx];
@@ -573,14 +584,15 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   constexpr int NCB = D / kCols;
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   // Consecutive workgroups are dispatched round-robin over the 8 XCDs; within
-  // each group of 8 * NCB, remap so that one XCD receives the NCB column blocks of
-  // one head (they share its operands through one L2), keeping the
-  // longest-sequence-first order between groups.
+  // each group of 8 * G * NCB, remap so that one XCD receives the NCB column blocks
+  // of the G value heads of one key head (they share its K and Q rows, and each
+  // head's units, through one L2), keeping the longest-sequence-first order
+  // between groups.
   int b = blockIdx.x;
-  const int nb = gridDim.x, grp = 8 * NCB;
+  const int nb = gridDim.x, per_xcd = G * NCB, grp = 8 * per_xcd;
   if (b < nb - nb % grp) {
     const int r = b % grp;
-    b = (b - r) + (r % 8) * NCB + r / 8;
+    b = (b - r) + (r % 8) * per_xcd + r / 8;
   }
   const int cb = b % NCB, hq = b / NCB, h = hq % Hv, q = hq / Hv;
   const int seq = tb.implicit ? 0 : tb.order[q];
