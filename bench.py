@@ -47,8 +47,8 @@ DECODE_TRAFFIC = {
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
     "sha256": "4268cd16915aa61e829dd975d27d51fa96da7cd3e03e560fdd0bf50495c19f0f",
-    "fetch_kib": 136039.3, "write_kib": 269312.0,
-    "fetch_scale": 1048576.0 / 524302.0, "write_scale": 1048576.0 / 1048576.0,
+    "fetch_kib": 136031.2, "write_kib": 269312.0,
+    "fetch_scale": 1048576.0 / 524301.8, "write_scale": 1048576.0 / 1048576.0,
 }
 
 
