@@ -56,7 +56,7 @@ def _wy_form(dims, state):
 @pytest.mark.parametrize("case,state", [("config3", "f32"), ("config3", "f16"), ("tiny_fp32", "f32"),
                                         ("edge_k", "f32"), ("n128_k1", "f32"), ("d64_g4", "f16"),
                                         ("d64_g4", "f32"), ("extreme_raw_gates", "f32"), ("g1_f32act", "f32"),
-                                        ("g4_d128_k3", "f32")])
+                                        ("g4_d128_k3", "f32"), ("repeat_keys", "f32")])
 def test_woa_verify_and_fold(case, state):
     """Outputs and stash against the oracle; the fold of the accepted rows against
     the oracle and against the state the write-all verify records after the same
@@ -85,6 +85,17 @@ def test_woa_verify_and_fold(case, state):
         d["b"] = rng.choice([-30.0, 0.0, 30.0], size=d["b"].shape).astype(np.float32)
         gates = "raw"
         sample = np.arange(6)
+    elif case == "repeat_keys":  # the same key in every row with a = b = 1: A's lower triangle all ones
+        d = W.verify_inputs(3121, 3, W.QWEN_DIMS, ks=[16, 9, 5])
+        dims0 = d["dims"]
+        kc = slice(dims0.Hk * dims0.dk, 2 * dims0.Hk * dims0.dk)  # pre-conv key channels
+        for i in range(3):
+            r0, r1 = int(d["cu"][i]), int(d["cu"][i + 1])
+            d["x"][r0:r1, kc] = d["x"][r0, kc]
+            d["ring"][i][:, kc] = d["x"][r0, kc]
+        d["a"][:] = 1.0
+        d["b"][:] = 1.0
+        sample = np.arange(3)
     elif case == "g1_f32act":  # one value head per key head, fp32 activations
         d = W.verify_inputs(3118, 5, W.Dims(Hk=4, Hv=4, dk=128, dv=128, K=4), act="f32", ks=[16, 3, 11, 1, 8])
         sample = np.arange(5)
