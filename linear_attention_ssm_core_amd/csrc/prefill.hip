@@ -757,17 +757,20 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       __syncthreads();
       bf16x8 xh[2][2], xl[2][2];
       load_xt(xh, xl);
+      // the four output tiles are independent accumulation chains: innermost, so
+      // that consecutive MFMAs never wait for each other's results
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int term = 0; term < 3; ++term)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 mh = as_bf16x8(mt[rt][ks]), ml = as_bf16x8(mt[rt][2 + ks]);
-            Ot[rt][ct] = mfma16(xh[ct][ks], mh, Ot[rt][ct]);
-            Ot[rt][ct] = mfma16(xl[ct][ks], mh, Ot[rt][ct]);
-            Ot[rt][ct] = mfma16(xh[ct][ks], ml, Ot[rt][ct]);
-          }
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const bf16x8 a = term == 1 ? xl[ct][ks] : xh[ct][ks];
+              const bf16x8 m = as_bf16x8(term == 2 ? mt[rt][2 + ks] : mt[rt][ks]);
+              Ot[rt][ct] = mfma16(a, m, Ot[rt][ct]);
+            }
       fetch_mt(cn);  // issued while the O products are in flight
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
@@ -824,15 +827,23 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          hacc[t][ct] *= gC;
+        for (int ct = 0; ct < 2; ++ct) hacc[t][ct] *= gC;
+      // four independent accumulation chains, innermost (see the O products)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 eh = as_bf16x8(ef[PAR][t][ks]), el = as_bf16x8(ef[PAR][t][2 + ks]);
-            hacc[t][ct] = mfma16(eh, xh[ct][ks], hacc[t][ct]);
-            hacc[t][ct] = mfma16(eh, xl[ct][ks], hacc[t][ct]);
-            hacc[t][ct] = mfma16(el, xh[ct][ks], hacc[t][ct]);
-          }
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int term = 0; term < 3; ++term)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const bf16x8 e = as_bf16x8(term == 2 ? ef[PAR][t][2 + ks] : ef[PAR][t][ks]);
+              hacc[t][ct] = mfma16(e, term == 1 ? xl[ct][ks] : xh[ct][ks], hacc[t][ct]);
+            }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
           const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
           store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
                        &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
