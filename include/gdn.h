@@ -188,6 +188,9 @@ gdn_status gdn_conv_l2norm(const gdn_conv_args *args, void *stream /* hipStream_
  *   _chunk_fwd_o_k handles (layer_struct.rs) and
  *   prefill_gdn_full_batched_fla_varlen (trait_layer.rs).
  *   Needs a caller-owned workspace of gdn_prefill_workspace_bytes() bytes.
+ *   With T = 0 (every sequence empty) the per-token arrays (a, b, x or y, z,
+ *   out) may be NULL and nothing changes; cu_seqlens and h_state are still
+ *   required for n > 0.
  * ------------------------------------------------------------------------- */
 typedef struct gdn_prefill_args {
   uint32_t struct_size;        /* sizeof(gdn_prefill_args)                      */

@@ -293,8 +293,9 @@ gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
   if (s != GDN_OK) return s;
   const int n = a->num_seqs;
   const int64_t T = a->total_tokens;
-  if (n > 0 && (a->cu_seqlens == nullptr || a->a == nullptr || a->b == nullptr || a->h_state == nullptr))
-    return GDN_ERR_INVALID_ARG;
+  if (n > 0 && (a->cu_seqlens == nullptr || a->h_state == nullptr)) return GDN_ERR_INVALID_ARG;
+  // per-token arrays are read only when there are tokens
+  if (T > 0 && (a->a == nullptr || a->b == nullptr)) return GDN_ERR_INVALID_ARG;
   if (T > 0 && a->out == nullptr) return GDN_ERR_INVALID_ARG;
   if (plan.fused_front && (a->conv_w == nullptr || a->conv_state == nullptr)) return GDN_ERR_INVALID_ARG;
   if (!plan.fused_front && T > 0 && a->y == nullptr) return GDN_ERR_INVALID_ARG;

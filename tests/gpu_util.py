@@ -44,12 +44,14 @@ def slice_err(gpu, ref, row_seq=None):
         diff = np.abs(gpu - ref).reshape(ref.shape[0], ref.shape[1], -1).max(axis=2)
         mag = np.abs(ref).reshape(ref.shape[0], ref.shape[1], -1).max(axis=2)
         return float(np.max(diff / np.maximum(mag, 1e-30)))
-    for s in np.unique(row_seq):
-        m = row_seq == s
-        diff = np.abs(gpu[m] - ref[m]).max(axis=(0, 2))
-        mag = np.abs(ref[m]).max(axis=(0, 2))
-        worst = max(worst, float(np.max(diff / np.maximum(mag, 1e-30))))
-    return worst
+    row_seq = np.asarray(row_seq)
+    if row_seq.size == 0:
+        return worst
+    # rows of one sequence are contiguous (packed batches): reduce each run of rows
+    starts = np.flatnonzero(np.r_[True, row_seq[1:] != row_seq[:-1]])
+    diff = np.maximum.reduceat(np.abs(gpu - ref).max(axis=2), starts, axis=0)
+    mag = np.maximum.reduceat(np.abs(ref).max(axis=2), starts, axis=0)
+    return float(np.max(diff / np.maximum(mag, 1e-30)))
 
 
 def row_seq_of(cu):
