@@ -9,7 +9,8 @@ q and k head is x (sum x^2 + l2_eps)^(-1/2), and the gated norm divides by
 the conv front, the chunked prefill with its fused front and norm, the one-token
 decode, the k-row verify (outputs and stored states), the write-on-accept verify
 in both of its forms (row loop at d = 32, WY form at d = 128), the k-token decode
-and the standalone gated norm."""
+and the standalone gated norm.  The multi-row modes are also run with an output
+scale and no gated norm (which would cancel the scale)."""
 import numpy as np
 import pytest
 import torch
@@ -152,3 +153,48 @@ def test_gated_rmsnorm_large_eps():
     B.gdn_gated_rmsnorm(tdev(o, F32), tdev(z, F32), tdev(w, F32), out, dims, eps=NORM_EPS)
     ref = oracle.gated_rmsnorm(o.reshape(T, dims.Hv, dims.dv), z.reshape(T, dims.Hv, dims.dv), w, eps=NORM_EPS)
     assert slice_err(host(out).reshape(T, dims.Hv, dims.dv), ref, np.arange(T)) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Output scale without the gated norm (the norm would cancel it): o = scale * S q
+# in the row-by-row verify, both write-on-accept forms and the k-token decode.
+# ---------------------------------------------------------------------------
+SCALE = 0.3
+
+
+@pytest.mark.parametrize("dims,act", CASES)
+def test_multi_row_modes_scale_without_norm(dims, act):
+    d, a_t = _verify_data(dims, act, 9700 + dims.dk)
+    n, ks, cu = d["n"], d["ks"], d["cu"]
+    T = int(cu[-1])
+    args = lambda: (tdev(d["x"], a_t), tdev(d["conv_w"], a_t))
+    ref = oracle.verify(d["x"], d["conv_w"], d["ring"], d["a"], d["b"], d["S0"], cu, dims.Hk, dims.Hv, dims.dk,
+                        dims.dv, scale=SCALE)
+    rows = row_seq_of(cu)
+
+    # row-by-row verify, every state stored
+    ds = DeviceStates(d["S0"], d["ring"], a_t)
+    inter = [[torch.empty((dims.Hv, dims.dk, dims.dv), device=DEV) for _ in range(ks[i] - 1)] for i in range(n)]
+    tables = [[None] * n for _ in range(16)]
+    for i in range(n):
+        tables[0][i] = ds.h[i]
+        for t in range(ks[i] - 1):
+            tables[t + 1][i] = inter[i][t]
+    out = torch.empty((T, dims.Hv * dims.dv), dtype=F32, device=DEV)
+    B.gdn_verify_multi(*args(), ds.ring_ptrs, tdev(d["a"], F32), tdev(d["b"], F32), B.wy_tables(tables, DEV),
+                       tdev(cu, torch.int32), int(ks.max()), out, dims, scale=SCALE)
+    assert slice_err(host(out).reshape(T, dims.Hv, dims.dv), ref["o"], rows) < TOL_OUT
+
+    # write-on-accept verify
+    ds = DeviceStates(d["S0"], d["ring"], a_t)
+    out = torch.empty((T, dims.Hv * dims.dv), dtype=F32, device=DEV)
+    B.gdn_verify_woa(*args(), ds.ring_ptrs, tdev(d["a"], F32), tdev(d["b"], F32), ds.h_ptrs, tdev(cu, torch.int32),
+                     int(ks.max()), out, dims, scale=SCALE)
+    assert slice_err(host(out).reshape(T, dims.Hv, dims.dv), ref["o"], rows) < TOL_OUT
+
+    # k-token decode (the same rows as consecutive tokens: the same outputs)
+    ds = DeviceStates(d["S0"], d["ring"], a_t)
+    out = torch.empty((T, dims.Hv * dims.dv), dtype=F32, device=DEV)
+    B.gdn_decode_tokens(*args(), ds.ring_ptrs, tdev(d["a"], F32), tdev(d["b"], F32), ds.h_ptrs,
+                        tdev(cu, torch.int32), int(ks.max()), out, dims, scale=SCALE)
+    assert slice_err(host(out).reshape(T, dims.Hv, dims.dv), ref["o"], rows) < TOL_OUT
