@@ -6,9 +6,15 @@ One step is one pass of the whole hot path over synthetic inputs resident in HBM
   prefill  T = 4096 tokens, 16 key / 32 value heads, d = 128, bf16 activations,
            fp32 state: gdn_conv_l2norm -> gdn_prefill_chunked -> gdn_gated_rmsnorm
   decode   128 sequences x 100 consecutive steps of gdn_decode_batched (fused
-           conv/L2 prologue and gated-norm epilogue, fp32 states in place)
+           conv/L2 prologue and gated-norm epilogue, fp32 states in place); the
+           100 launches cycle over DECODE_LAYERS = 4 disjoint sets of the 128
+           sequences' states and conv states (the per-layer states of a 4-layer
+           stack: 1 GiB of fp32 state, four times the 256 MB on-package cache), so
+           every launch streams its states from HBM
   verify   64 sequences, draft lengths k ~ U{2..16}: gdn_verify_multi writing every
-           intermediate state through the WY tables, then gdn_verify_commit
+           intermediate state through the WY tables, then gdn_verify_commit; the
+           sequence states and conv states alternate between two sets from one
+           step to the next
 
 value = tokens processed per step / step time (prefill tokens + decode
 sequence-tokens + verify rows).  The JSON line also carries per-phase figures,
@@ -33,6 +39,8 @@ VALU_FP32_PEAK = 157.3e12   # FLOP/s, MI355X fp32 vector (packed issue; half wit
 D, HK, HV, C = 128, 16, 32, 64
 STATE_BYTES = HV * D * D * 4            # one sequence's fp32 state, 2 MiB
 CONV_DIM = 2 * HK * D + HV * D          # 8192
+DECODE_LAYERS = 4                       # disjoint state sets the decode launches cycle over
+VERIFY_SETS = 2                         # state sets the verify/commit alternate between
 
 
 # HBM traffic of one decode launch (recurrent_kernel<128,2,1>), from two rocprofv3
@@ -175,9 +183,12 @@ class Workloads:
         self.d_b = t(d["b"], f32)
         self.d_w = t(d["conv_w"], bf)
         self.d_nw = t(d["norm_w"], bf)
-        self.d_h = [t(d["S0"][i], f32) for i in range(self.d_n)]
-        self.d_ring = [t(d["ring"][i], bf) for i in range(self.d_n)]
-        self.d_hp, self.d_rp = B.ptr_array(self.d_h), B.ptr_array(self.d_ring)
+        # DECODE_LAYERS disjoint sets of states and conv states (each starts from the
+        # workload's initial values); launch s uses set s % DECODE_LAYERS
+        self.d_h = [[t(d["S0"][i], f32) for i in range(self.d_n)] for _ in range(DECODE_LAYERS)]
+        self.d_ring = [[t(d["ring"][i], bf) for i in range(self.d_n)] for _ in range(DECODE_LAYERS)]
+        self.d_hp = [B.ptr_array(hs) for hs in self.d_h]
+        self.d_rp = [B.ptr_array(rs) for rs in self.d_ring]
         self.d_out = torch.empty((self.d_n, HV * D), dtype=bf, device=dev)
         # verify (64 sequences, k ~ U{2..16}) and commit
         v = W.config(3)
@@ -190,24 +201,30 @@ class Workloads:
         self.v_b = t(v["b"], f32)
         self.v_w = t(v["conv_w"], bf)
         self.v_nw = t(v["norm_w"], bf)
-        self.v_h = [t(v["S0"][i], f32) for i in range(self.v_n)]
-        self.v_ring = [t(v["ring"][i], bf) for i in range(self.v_n)]
-        self.v_rp = B.ptr_array(self.v_ring)
+        # VERIFY_SETS sets of sequence states (table 0) and conv states, alternating
+        # per step; the intermediate-state buffers are shared (written, then read by
+        # the commit of the same step)
+        self.v_h = [[t(v["S0"][i], f32) for i in range(self.v_n)] for _ in range(VERIFY_SETS)]
+        self.v_ring = [[t(v["ring"][i], bf) for i in range(self.v_n)] for _ in range(VERIFY_SETS)]
+        self.v_rp = [B.ptr_array(rs) for rs in self.v_ring]
         self.v_inter = [[torch.empty((HV, D, D), dtype=f32, device=dev) for _ in range(k - 1)] for k in self.v_ks]
-        tables = [[None] * self.v_n for _ in range(16)]
-        for i in range(self.v_n):
-            tables[0][i] = self.v_h[i]
-            for j, buf in enumerate(self.v_inter[i]):
-                tables[j + 1][i] = buf
-        self.v_tab = B.wy_tables(tables, dev)
+        self.v_tab = []
+        for hs in self.v_h:
+            tables = [[None] * self.v_n for _ in range(16)]
+            for i in range(self.v_n):
+                tables[0][i] = hs[i]
+                for j, buf in enumerate(self.v_inter[i]):
+                    tables[j + 1][i] = buf
+            self.v_tab.append(B.wy_tables(tables, dev))
         self.v_out = torch.empty((self.v_rows, HV * D), dtype=bf, device=dev)
         self.v_nacc = t(v["n_acc"], torch.int32)
         self.v_maxk = int(self.v_ks.max())
         self.tokens_per_step = self.p_T + self.d_n * self.d_steps + self.v_rows
 
 
-def run_step(torch, B, w, ev=None):
-    """One pass of the hot path.  ev: dict of lists that receives HIP events."""
+def run_step(torch, B, w, step, ev=None):
+    """One pass of the hot path (step: its index, which picks the verify's state
+    set).  ev: dict of lists that receives HIP events."""
     rec = (lambda key: ev[key].append(_event(torch))) if ev is not None else (lambda key: None)
     dims = w.dims
     rec("p0")
@@ -222,14 +239,16 @@ def run_step(torch, B, w, ev=None):
     # pair's interval over the launch count
     rec("d0")
     for s in range(w.d_steps):
-        B.gdn_decode_batched(w.d_x[s], w.d_w, w.d_rp, w.d_a[s], w.d_b[s], w.d_hp, w.d_out, dims,
+        L = s % DECODE_LAYERS
+        B.gdn_decode_batched(w.d_x[s], w.d_w, w.d_rp[L], w.d_a[s], w.d_b[s], w.d_hp[L], w.d_out, dims,
                              z=w.d_z[s], norm_w=w.d_nw)
     rec("d1")
+    vs = step % VERIFY_SETS
     rec("v0")
-    B.gdn_verify_multi(w.v_x, w.v_w, w.v_rp, w.v_a, w.v_b, w.v_tab, w.v_cu, w.v_maxk, w.v_out, dims,
+    B.gdn_verify_multi(w.v_x, w.v_w, w.v_rp[vs], w.v_a, w.v_b, w.v_tab[vs], w.v_cu, w.v_maxk, w.v_out, dims,
                        z=w.v_z, norm_w=w.v_nw)
     rec("v1")
-    B.gdn_verify_commit(w.v_x, w.v_rp, w.v_tab, w.v_cu, w.v_nacc, dims)
+    B.gdn_verify_commit(w.v_x, w.v_rp[vs], w.v_tab[vs], w.v_cu, w.v_nacc, dims)
     rec("v2")
 
 
@@ -253,16 +272,25 @@ def variant_phases(torch, B, W, w, reps=10):
     dims = w.dims
     res = {}
     v = W.config(3)
-    h = [torch.from_numpy(v["S0"][i]).to(f32).to(dev) for i in range(w.v_n)]
-    hp = B.ptr_array(h)
-    ring = [torch.from_numpy(v["ring"][i]).to(bf).to(dev) for i in range(w.v_n)]
-    rp = B.ptr_array(ring)
+    # DECODE_LAYERS disjoint state sets, used in turn by consecutive calls, so that no
+    # call finds its 128 MiB of states in the on-package cache
+    nset = DECODE_LAYERS
+    h = [[torch.from_numpy(v["S0"][i]).to(f32).to(dev) for i in range(w.v_n)] for _ in range(nset)]
+    hp = [B.ptr_array(hs) for hs in h]
+    ring = [[torch.from_numpy(v["ring"][i]).to(bf).to(dev) for i in range(w.v_n)] for _ in range(nset)]
+    rp = [B.ptr_array(rs) for rs in ring]
     stash = torch.empty(max(B.gdn_woa_stash_bytes(w.v_x, w.v_cu, w.v_maxk, w.v_out, dims) // 4, 1),
                         dtype=f32, device=dev)
-    woa = lambda: B.gdn_verify_woa(w.v_x, w.v_w, rp, w.v_a, w.v_b, hp, w.v_cu, w.v_maxk, w.v_out, dims,
-                                   stash=stash, z=w.v_z, norm_w=w.v_nw)
-    fold = lambda: B.gdn_fold_accepted(w.v_x, rp, hp, stash, w.v_cu, w.v_nacc, dims)
-    ms_v, ms_f = _timed(torch, woa, reps), _timed(torch, fold, reps)
+    turn = [0]
+
+    def nxt():
+        turn[0] += 1
+        return turn[0] % nset
+    woa = lambda j: B.gdn_verify_woa(w.v_x, w.v_w, rp[j], w.v_a, w.v_b, hp[j], w.v_cu, w.v_maxk, w.v_out, dims,
+                                     stash=stash, z=w.v_z, norm_w=w.v_nw)
+    fold = lambda j: B.gdn_fold_accepted(w.v_x, rp[j], hp[j], stash, w.v_cu, w.v_nacc, dims)
+    ms_v = _timed(torch, lambda: woa(nxt()), reps)
+    ms_f = _timed(torch, lambda: fold(nxt()), reps)
     vb, fb = woa_verify_bytes(w.v_ks), fold_bytes(v["n_acc"])
     # k-token decode, row by row in fp32: S k and S q (2 d^2 each), S <- a S + u k^T (3 d^2)
     # per row and value head, reported as a rate against the vector-ALU peak (its bound is
@@ -272,14 +300,15 @@ def variant_phases(torch, B, W, w, reps=10):
     valu = lambda ms: {"tflops": row_flops / (ms / 1e3) / 1e12,
                        "frac": row_flops / (ms / 1e3) / VALU_FP32_PEAK,
                        "frac_unpacked": row_flops / (ms / 1e3) / (VALU_FP32_PEAK / 2)}
+    print("bench: write-on-accept verify and fold timed", file=sys.stderr, flush=True)
     res["verify_woa"] = {"rows": w.v_rows, "ms": ms_v, "fold_ms": ms_f, "tokens_per_s": w.v_rows / (ms_v / 1e3),
                          "gb_per_s": vb / (ms_v / 1e3) / 1e9, "hbm_frac": vb / (ms_v / 1e3) / HBM_PEAK,
                          "fold_gb_per_s": fb / (ms_f / 1e3) / 1e9, "fold_hbm_frac": fb / (ms_f / 1e3) / HBM_PEAK,
                          "bytes": vb, "fold_bytes": fb, "bound": "hbm"}
     # k consecutive tokens per sequence on the verify's rows (state written once)
-    toks = lambda: B.gdn_decode_tokens(w.v_x, w.v_w, rp, w.v_a, w.v_b, hp, w.v_cu, w.v_maxk, w.v_out, dims,
-                                       z=w.v_z, norm_w=w.v_nw)
-    ms_t = _timed(torch, toks, reps)
+    toks = lambda j: B.gdn_decode_tokens(w.v_x, w.v_w, rp[j], w.v_a, w.v_b, hp[j], w.v_cu, w.v_maxk, w.v_out,
+                                         dims, z=w.v_z, norm_w=w.v_nw)
+    ms_t = _timed(torch, lambda: toks(nxt()), reps)
     tb = tokens_bytes(w.v_ks)
     res["decode_tokens"] = {"rows": w.v_rows, "ms": ms_t, "tokens_per_s": w.v_rows / (ms_t / 1e3),
                             "gb_per_s": tb / (ms_t / 1e3) / 1e9, "hbm_frac": tb / (ms_t / 1e3) / HBM_PEAK,
@@ -287,32 +316,48 @@ def variant_phases(torch, B, W, w, reps=10):
     del h, stash
     # binary16 states: the decode workload, 100 steps
     d = W.config(2)
-    h16 = [torch.from_numpy(d["S0"][i]).to(f16).to(dev) for i in range(w.d_n)]
-    hp16 = B.ptr_array(h16)
+    h16 = [[torch.from_numpy(d["S0"][i]).to(f16).to(dev) for i in range(w.d_n)] for _ in range(DECODE_LAYERS)]
+    hp16 = [B.ptr_array(hs) for hs in h16]
     opt16 = B.options(f16)
 
     def dec16():
         for s_ in range(w.d_steps):
-            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp, w.d_a[s_], w.d_b[s_], hp16, w.d_out, dims,
+            L = s_ % DECODE_LAYERS
+            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp[L], w.d_a[s_], w.d_b[s_], hp16[L], w.d_out, dims,
                                  z=w.d_z[s_], norm_w=w.d_nw, opt=opt16)
     ms16 = _timed(torch, dec16, 1) / w.d_steps
     db16 = w.d_n * (decode_bytes_per_seq() - STATE_BYTES) + CONV_DIM * 4 * 2 + D * 2
     res["decode_f16_state"] = {"ms_per_launch": ms16, "tokens_per_s": w.d_n / (ms16 / 1e3),
                                "gb_per_s": db16 / (ms16 / 1e3) / 1e9, "hbm_frac": db16 / (ms16 / 1e3) / HBM_PEAK}
     del h16
-    # raw gate inputs and the sigmoid-gated norm (the fp32-state decode otherwise)
+    # raw gate inputs and the sigmoid-gated norm (the fp32-state decode otherwise,
+    # cycling over the step's state sets)
     optg = B.options(None, gates="raw", norm_gate="sigmoid")
 
     def decg():
         for s_ in range(w.d_steps):
-            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp, w.d_a[s_], w.d_b[s_], w.d_hp, w.d_out, dims,
+            L = s_ % DECODE_LAYERS
+            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp[L], w.d_a[s_], w.d_b[s_], w.d_hp[L], w.d_out, dims,
                                  z=w.d_z[s_], norm_w=w.d_nw, opt=optg)
     msg = _timed(torch, decg, 1) / w.d_steps
     db = w.d_n * decode_bytes_per_seq() + CONV_DIM * 4 * 2 + D * 2
     res["decode_raw_gates_sigmoid_norm"] = {"ms_per_launch": msg, "gb_per_s": db / (msg / 1e3) / 1e9,
                                             "hbm_frac": db / (msg / 1e3) / HBM_PEAK}
-    # the varlen packed prefill: 8 sequences, log-uniform lengths, one call with the
-    # conv + L2 front and the gated-norm epilogue fused
+    # the same 128 states re-read and re-written by all 100 launches (256 MiB, about
+    # the size of the on-package cache, which can serve part of the traffic): the
+    # cache-warm figure, for comparison with the step's cache-cold one
+
+    def dec_warm():
+        for s_ in range(w.d_steps):
+            B.gdn_decode_batched(w.d_x[s_], w.d_w, w.d_rp[0], w.d_a[s_], w.d_b[s_], w.d_hp[0], w.d_out, dims,
+                                 z=w.d_z[s_], norm_w=w.d_nw)
+    msw = _timed(torch, dec_warm, 1) / w.d_steps
+    res["decode_cache_warm"] = {"ms_per_launch": msw, "gb_per_s": db / (msw / 1e3) / 1e9,
+                                "hbm_frac": db / (msw / 1e3) / HBM_PEAK,
+                                "note": "one set of 128 states (256 MiB) for all 100 launches"}
+    print("bench: decode variants timed; generating the varlen prefill inputs", file=sys.stderr, flush=True)
+    # the varlen packed prefill: 8 sequences, log-uniform lengths totalling about
+    # 65,536 tokens, one call with the conv + L2 front and the gated-norm epilogue fused
     p = W.config(4)
     T4 = int(p["cu"][-1])
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
@@ -478,8 +523,8 @@ def main():
     w = Workloads(torch, B, W)
     print("bench: inputs resident; warmup %d, timed %d steps" % (args.warmup, args.steps), file=sys.stderr,
           flush=True)
-    for _ in range(args.warmup):
-        run_step(torch, B, w)
+    for i in range(args.warmup):
+        run_step(torch, B, w, i)
     torch.cuda.synchronize()
 
     keys = ["p0", "p1", "p2", "p3", "d0", "d1", "v0", "v1", "v2"]
@@ -488,8 +533,8 @@ def main():
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
-        run_step(torch, B, w, ev)
+    for i in range(args.steps):
+        run_step(torch, B, w, args.warmup + i, ev)
     stop.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -537,10 +582,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; shapes of the five GDN workloads)",
         "config": {"workload": "GDN mixer core step: prefill T=4096 (16/32 heads, d=128, chunk 64) + "
-                               "batched decode 128 seqs x 100 steps + speculative verify/commit 64 seqs "
-                               "k~U{2..16}", "tokens_per_step": w.tokens_per_step,
-                   "verify_rows": w.v_rows},
-        "roofline": {"bound": "hbm", "kernel": "gdn_decode_batched (recurrent_kernel<128,2,1>)",
+                               "batched decode 128 seqs x 100 steps (over %d layers' state sets, cache-cold) + "
+                               "speculative verify/commit 64 seqs k~U{2..16}" % DECODE_LAYERS,
+                   "tokens_per_step": w.tokens_per_step, "verify_rows": w.v_rows,
+                   "decode_state_sets": DECODE_LAYERS, "verify_state_sets": VERIFY_SETS},
+        "roofline": {"bound": "hbm", "kernel": "gdn_decode_batched (recurrent_kernel<128,2,1>), cache-cold: "
+                                               "%d state sets of 256 MiB cycled" % DECODE_LAYERS,
                      "achieved": dec_gbs, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": dec_gbs * 1e9 / HBM_PEAK,
                      "traffic": None if dec_traffic is None else dec_traffic / (float(np.mean(dec_ms)) / 1e3) / 1e9,

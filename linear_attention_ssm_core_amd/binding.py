@@ -12,7 +12,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgdn.so")
+# GDN_LIBRARY names another build of the same library (an instrumented host
+# build, say); by default the in-tree libgdn.so is loaded.
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
 GDN_DTYPE_F32, GDN_DTYPE_BF16, GDN_DTYPE_F16 = 0, 1, 2
@@ -24,8 +26,8 @@ PREFILL_CHUNK = 64
 DECODE_MAX_TOKENS = 17
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libgdn.so is not built (run `python -m linear_attention_ssm_core_amd.build`); "
-                      "there is no fallback path")
+    raise ImportError("%s is not built (run `python -m linear_attention_ssm_core_amd.build`); "
+                      "there is no fallback path" % LIB_PATH)
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp = ctypes.c_void_p

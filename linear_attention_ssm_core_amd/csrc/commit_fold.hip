@@ -7,9 +7,12 @@
 namespace gdn {
 namespace {
 
-// blockIdx.y < kCommitSplit: one eighth of the state copy, 8 loads in flight per
-// thread; otherwise conv-state channels.
-constexpr int kCommitSplit = 8;
+// The state copy of a sequence is split into tiles of 256 threads x 8 16-byte
+// vectors (32 KiB, 8 loads in flight per thread), one workgroup each: 64
+// workgroups per 2 MiB state, so the ~50 copies of a verify batch spread over the
+// whole chip.  blockIdx.y < the tile count copies a tile; the rest rebuild
+// conv-state channels.
+constexpr int kCommitTile = 256 * 8;  // 16-byte vectors per copy workgroup
 constexpr int kMaxFoldRows = 16;
 
 // The conv state of sequence i becomes the last K-1 rows of
@@ -36,30 +39,28 @@ __device__ __forceinline__ void advance_ring(const Geometry &geo, void *const *c
 
 // Commit: copy the state after the last accepted row into table 0.
 template <typename TE>
-__global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4) {
+__global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4, int ntiles) {
   const int i = blockIdx.x;
   const int k = p.cu[i + 1] - p.cu[i];
   const int na = p.n_accepted[i];
   if (na < 1 || na > k) return;  // outside the caller's contract: sequence untouched
-  if ((int)blockIdx.y < kCommitSplit) {
+  if ((int)blockIdx.y < ntiles) {
     if (na == k) return;  // table 0 already holds the last state
     // (native 4-float vectors: the struct-based float4 array ends up in scratch)
     const gptr<const floatx4> src = to_global(static_cast<const floatx4 *>(p.tables[na * kTableSeqs + i]));
     const gptr<floatx4> dst = to_global(static_cast<floatx4 *>(p.tables[i]));
-    const int64_t per = (n4 + kCommitSplit - 1) / kCommitSplit;
-    const int64_t beg = (int64_t)blockIdx.y * per, end = min(n4, beg + per);
-    // whole tiles of 256 x 8 vectors without conditions, then the tail
-    int64_t i0 = beg;
-    for (; i0 + 256 * 8 <= end; i0 += 256 * 8) {
+    const int64_t beg = (int64_t)blockIdx.y * kCommitTile;
+    if (beg + kCommitTile <= n4) {  // a whole tile, without conditions
       floatx4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[i0 + threadIdx.x + u * 256];
+      for (int u = 0; u < 8; ++u) v[u] = src[beg + threadIdx.x + u * 256];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) dst[i0 + threadIdx.x + u * 256] = v[u];
+      for (int u = 0; u < 8; ++u) dst[beg + threadIdx.x + u * 256] = v[u];
+    } else {
+      for (int64_t idx = beg + threadIdx.x; idx < n4; idx += 256) dst[idx] = src[idx];
     }
-    for (int64_t idx = i0 + threadIdx.x; idx < end; idx += 256) dst[idx] = src[idx];
   } else {
-    advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.y - kCommitSplit);
+    advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.y - ntiles);
   }
 }
 
@@ -133,12 +134,13 @@ hipError_t launch_commit(const CommitLaunch &p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;
   // 16-byte vectors per sequence state: 4 fp32 or 8 binary16 elements each
   const int64_t n4 = (int64_t)p.geo.Hv * p.geo.D * p.geo.D / (p.state_f16 ? 8 : 4);
+  const int ntiles = (int)((n4 + kCommitTile - 1) / kCommitTile);
   const int nblk_ring = (p.geo.conv_dim + 255) / 256;
-  const dim3 grid(p.n, kCommitSplit + nblk_ring), block(256);
+  const dim3 grid(p.n, ntiles + nblk_ring), block(256);
   if (p.geo.act_bf16)
-    hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, n4);
+    hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, n4, ntiles);
   else
-    hipLaunchKernelGGL((commit_kernel<float>), grid, block, 0, stream, p, n4);
+    hipLaunchKernelGGL((commit_kernel<float>), grid, block, 0, stream, p, n4, ntiles);
   return hipGetLastError();
 }
 

@@ -36,7 +36,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.LIB
+        # GDN_ORACLE_LIBRARY names another build of gdn_oracle.c (an instrumented
+        # one, say); by default the in-tree build
+        path = os.environ.get("GDN_ORACLE_LIBRARY") or _build.LIB
         if not os.path.exists(path):
             _build.build(force=True)
         _lib = load_library(path)

@@ -86,14 +86,15 @@ def test_prefill_config1_single_sequence():
 
 
 def test_prefill_config4_varlen_fused():
-    """8 sequences, log-uniform lengths in 512..32768, fused conv/L2 front and
-    Z-gated RMSNorm epilogue in one call; 3 of 32 heads checked against the
-    oracle from the pre-conv rows (the front stays fp32 end to end)."""
+    """8 sequences, log-uniform lengths in 512..32768 totalling 64,831 tokens,
+    fused conv/L2 front and Z-gated RMSNorm epilogue in one call; every head,
+    every output row and every final state against the oracle from the pre-conv
+    rows (the front stays fp32 end to end)."""
     d = W.config(4)
-    heads = [0, 13, 31]
+    assert abs(int(d["cu"][-1]) - W.VARLEN_TARGET_TOKENS) <= 0.05 * W.VARLEN_TARGET_TOKENS
     out, ds, _ = _run(d, fused=True, epilogue=True)
-    ref = _ref(d, heads=heads, epilogue=True)
-    _check(d, out, ds, ref, heads=heads)
+    ref = _ref(d, epilogue=True)
+    _check(d, out, ds, ref)
 
 
 @pytest.mark.parametrize("dims,act", [(W.Dims(Hk=2, Hv=4, dk=128, dv=128), "bf16"),
@@ -111,7 +112,7 @@ def test_prefill_ragged_and_empty(dims, act):
 
 
 @pytest.mark.parametrize("dims,act,n,heads", [(W.TINY_DIMS, "f32", 200, None),
-                                              (W.QWEN_DIMS, "bf16", 40, [0, 17, 31])])
+                                              (W.QWEN_DIMS, "bf16", 40, None)])
 def test_prefill_many_short_sequences(dims, act, n, heads):
     """Batches of many short sequences (0..150 rows): the chunk table, the
     longest-first order and one spine workgroup set per sequence."""
