@@ -230,6 +230,26 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_prefill_args *args, size_t *byt
 gdn_status gdn_prefill_chunked(const gdn_prefill_args *args, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * gdn_prefill_chunked_noalloc -- gdn_prefill_chunked without a caller workspace
+ *   and without any allocation, for callers that cannot allocate device memory:
+ *   code under HIP graph capture, tight serving loops, harnesses that forbid
+ *   allocation.  Same arguments, results and validation as gdn_prefill_chunked,
+ *   except: workspace must be NULL and workspace_bytes 0 (else
+ *   GDN_ERR_INVALID_ARG), and the workspace the call needs
+ *   (gdn_prefill_workspace_bytes) must not exceed GDN_PREFILL_SCRATCH_BYTES (else
+ *   GDN_ERR_WORKSPACE; nothing launched).  The call runs in a library-owned device
+ *   array of GDN_PREFILL_SCRATCH_BYTES bytes, one per GPU, present from the
+ *   library's load on that GPU until the process ends; its address is looked up
+ *   on the first call on each device.  Every call on one GPU uses the same array:
+ *   calls that overlap on one GPU (other streams, other threads) race and must be
+ *   serialised by the caller.  Returns GDN_ERR_HIP if the array's address cannot
+ *   be obtained.
+ * ------------------------------------------------------------------------- */
+#define GDN_PREFILL_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_prefill_args *args, void *stream);
+
+/* ---------------------------------------------------------------------------
  * gdn_decode_batched -- one token for each of n sequences, one launch.
  *   Per sequence: conv of one row with its conv state (which advances), L2 of q
  *   and k, then per value head  kv = S k;  u = b (v - a kv);  S <- a S + u k^T;

@@ -117,6 +117,7 @@ class gdn_tokens_args(ctypes.Structure):
 
 
 for _name, _st in [("gdn_conv_l2norm", gdn_conv_args), ("gdn_prefill_chunked", gdn_prefill_args),
+                   ("gdn_prefill_chunked_noalloc", gdn_prefill_args),
                    ("gdn_decode_batched", gdn_decode_args), ("gdn_verify_multi", gdn_verify_args),
                    ("gdn_verify_commit", gdn_commit_args), ("gdn_gated_rmsnorm", gdn_norm_args),
                    ("gdn_verify_woa", gdn_woa_args), ("gdn_fold_accepted", gdn_fold_args),
@@ -268,6 +269,16 @@ def gdn_prefill_chunked(dims, cu_seqlens, a, b, h_state_ptrs, out, *, workspace=
     args = _prefill_args(dims, cu_seqlens, a, b, h_state_ptrs, out, workspace=workspace, **kw)
     _check(_lib.gdn_prefill_chunked(ctypes.byref(args), _stream(stream)))
     return workspace
+
+
+PREFILL_SCRATCH_BYTES = 64 << 20
+
+
+def gdn_prefill_chunked_noalloc(dims, cu_seqlens, a, b, h_state_ptrs, out, *, stream=None, **kw):
+    """gdn_prefill_chunked in the library's own per-GPU scratch array (no workspace,
+    no allocation); the call's workspace need must fit PREFILL_SCRATCH_BYTES."""
+    args = _prefill_args(dims, cu_seqlens, a, b, h_state_ptrs, out, **kw)
+    _check(_lib.gdn_prefill_chunked_noalloc(ctypes.byref(args), _stream(stream)))
 
 
 def _opt(opt):

@@ -287,9 +287,13 @@ gdn_status gdn_prefill_workspace_bytes(const gdn_prefill_args *a, size_t *bytes)
   return GDN_OK;
 }
 
-gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
-  PrefillPlan plan;
-  gdn_status s = plan_prefill(a, &plan);
+}  // extern "C"
+
+namespace {
+
+// Validation shared by both prefill entry points (everything but the workspace).
+gdn_status check_prefill(const gdn_prefill_args *a, PrefillPlan *plan) {
+  gdn_status s = plan_prefill(a, plan);
   if (s != GDN_OK) return s;
   const int n = a->num_seqs;
   const int64_t T = a->total_tokens;
@@ -297,16 +301,17 @@ gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
   // per-token arrays are read only when there are tokens
   if (T > 0 && (a->a == nullptr || a->b == nullptr)) return GDN_ERR_INVALID_ARG;
   if (T > 0 && a->out == nullptr) return GDN_ERR_INVALID_ARG;
-  if (plan.fused_front && (a->conv_w == nullptr || a->conv_state == nullptr)) return GDN_ERR_INVALID_ARG;
-  if (!plan.fused_front && T > 0 && a->y == nullptr) return GDN_ERR_INVALID_ARG;
-  if (plan.epilogue && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  if (plan->fused_front && (a->conv_w == nullptr || a->conv_state == nullptr)) return GDN_ERR_INVALID_ARG;
+  if (!plan->fused_front && T > 0 && a->y == nullptr) return GDN_ERR_INVALID_ARG;
+  if (plan->epilogue && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
   if (n > 65535) return GDN_ERR_INVALID_ARG;
-  if (plan.total > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.total))
-    return GDN_ERR_WORKSPACE;
-  if (n == 0) return GDN_OK;
+  return GDN_OK;
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char *ws = static_cast<char *>(a->workspace);
+// The launches of a validated prefill on the workspace ws (plan.total bytes).
+gdn_status run_prefill(const gdn_prefill_args *a, const PrefillPlan &plan, char *ws, hipStream_t st) {
+  const int n = a->num_seqs;
+  const int64_t T = a->total_tokens;
   const Geometry &g = plan.geo;
 
   const void *y = a->y;
@@ -364,6 +369,34 @@ gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
   return GDN_OK;
+}
+
+static_assert(gdn::kPrefillScratchBytes == GDN_PREFILL_SCRATCH_BYTES, "scratch size of the header");
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_prefill_chunked(const gdn_prefill_args *a, void *stream) {
+  PrefillPlan plan;
+  gdn_status s = check_prefill(a, &plan);
+  if (s != GDN_OK) return s;
+  if (plan.total > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.total))
+    return GDN_ERR_WORKSPACE;
+  if (a->num_seqs == 0) return GDN_OK;
+  return run_prefill(a, plan, static_cast<char *>(a->workspace), static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_prefill_args *a, void *stream) {
+  PrefillPlan plan;
+  gdn_status s = check_prefill(a, &plan);
+  if (s != GDN_OK) return s;
+  if (a->workspace != nullptr || a->workspace_bytes != 0) return GDN_ERR_INVALID_ARG;
+  if (plan.total > gdn::kPrefillScratchBytes) return GDN_ERR_WORKSPACE;
+  if (a->num_seqs == 0) return GDN_OK;
+  void *ws = nullptr;
+  if (gdn::prefill_scratch(&ws) != hipSuccess) return GDN_ERR_HIP;
+  return run_prefill(a, plan, static_cast<char *>(ws), static_cast<hipStream_t>(stream));
 }
 
 gdn_status gdn_woa_stash_bytes(const gdn_woa_args *a, size_t *bytes) {

@@ -113,4 +113,10 @@ struct PrefillLaunch {
 size_t prefill_core_workspace(const Geometry &geo, int n, int64_t T);
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 
+// Scratch of the allocation-free prefill: a device array of this many bytes per
+// GPU, defined in prefill.hip.  prefill_scratch() returns its device address on
+// the current device (looked up once per device; no allocation).
+constexpr size_t kPrefillScratchBytes = size_t(64) << 20;
+hipError_t prefill_scratch(void **ptr);
+
 }  // namespace gdn

@@ -40,6 +40,8 @@
 // Precision: fp32-derived operands (h, X, T, E, MT, and fp32 activations) enter
 // MFMA as bf16 hi + lo; a product takes hi*hi + hi*lo + lo*hi, about 2^-16
 // relative, which keeps states within 1e-4 of the fp64 recurrence.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -913,6 +915,42 @@ hipError_t launch_prefill_y(const PrefillLaunch &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// ---- scratch of the allocation-free prefill ---------------------------------
+// The workspace of gdn_prefill_chunked_noalloc: one copy of this array on every
+// GPU that loads the library, held until the process ends.  Calls on one GPU share
+// it (overlapping calls race) and it keeps the last call's contents; no byte of it
+// needs to start at zero, since each call writes everything it reads first.  On
+// the host the name is only a stand-in for the device symbol: host code passes the
+// address hipGetSymbolAddress returns for the current device, cached per device.
+static __device__ __align__(256) char scratch[kPrefillScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t prefill_scratch(void **ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t prefill_core_workspace(const Geometry &geo, int n, int64_t T) {
   const int64_t NC = max_chunks(n, T);

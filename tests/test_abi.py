@@ -199,6 +199,26 @@ def test_prefill_validation_and_workspace():
     assert L.gdn_prefill_chunked(ctypes.byref(ok), None) == B.GDN_OK
 
 
+def test_prefill_noalloc_refusals():
+    """The allocation-free prefill validates like gdn_prefill_chunked, refuses a
+    workspace argument, and refuses a call whose workspace need exceeds its
+    per-GPU scratch array -- all before any HIP call."""
+    L = B.library()
+    call = lambda **kw: L.gdn_prefill_chunked_noalloc(ctypes.byref(_prefill_args(**kw)), None)
+    assert B.PREFILL_SCRATCH_BYTES == 64 << 20
+    # 512 tokens of 32 heads at d = 128 need about 24 MB; 4096 tokens about 101 MB
+    assert _ws(_prefill_args(total_tokens=512))[1] <= B.PREFILL_SCRATCH_BYTES
+    assert _ws(_prefill_args(total_tokens=4096))[1] > B.PREFILL_SCRATCH_BYTES
+    assert call(total_tokens=4096) == B.GDN_ERR_WORKSPACE
+    assert call(total_tokens=512, workspace=FAKE, workspace_bytes=1 << 30) == B.GDN_ERR_INVALID_ARG
+    assert call(total_tokens=512, workspace_bytes=1) == B.GDN_ERR_INVALID_ARG
+    assert call(total_tokens=512, chunk_size=32) == B.GDN_ERR_UNSUPPORTED
+    assert call(total_tokens=512, y=None) == B.GDN_ERR_INVALID_ARG
+    assert call(total_tokens=512, h_state=None) == B.GDN_ERR_INVALID_ARG
+    assert call(total_tokens=512, dims=_dims(d=80)) == B.GDN_ERR_UNSUPPORTED
+    assert call(num_seqs=0, total_tokens=0) == B.GDN_OK
+
+
 def test_options_are_refused_where_not_taken():
     """Every entry point validates its options before any launch: an unknown value,
     the reserved word, or an option the entry point does not take."""
