@@ -87,6 +87,19 @@ __device__ __forceinline__ void split_bf16(float x, bf16 &hi, bf16 &lo) {
   hi = (bf16)x;
   lo = (bf16)(x - (float)hi);
 }
+// The same split of two values as packed words (element 0 in the low half), with
+// one packed conversion per pair (widening a bf16 back to fp32 is exact: it only
+// appends zero bits).
+struct Split2 {
+  uint32_t hi, lo;
+};
+__device__ __forceinline__ Split2 split_bf16_2(float x0, float x1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float floatx2 __attribute__((ext_vector_type(2)));
+  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{x0, x1}, bf16x2));
+  const float f0 = __builtin_bit_cast(float, hb << 16), f1 = __builtin_bit_cast(float, hb & 0xffff0000u);
+  return {hb, __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{x0 - f0, x1 - f1}, bf16x2))};
+}
 
 // D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16) on the matrix cores.
 // Lane l holds A row (l % 16), B column (l % 16), and the 8 k-elements of group

@@ -32,11 +32,14 @@
 //      then E and MT on MFMA.  E and MT go to the workspace as bf16 hi/lo pairs in MFMA
 //      fragment order, so the next kernel loads each fragment as one contiguous 1 KiB
 //      block.
-//   3. spine_kernel, one workgroup per (sequence, value head, 32-column block of d_v):
-//      the serial pass over the chunks with specialised waves (K rows, Q rows, state
-//      owners); see the comment at the kernel.  Columns of h evolve independently, so a
-//      128-wide state splits into 4 workgroups; those of the value heads of one key
-//      head are mapped onto one XCD so they share its operands through one L2.
+//   3. spine_kernel, one workgroup per (sequence, value head, 16-column block of d_v):
+//      the serial pass over the chunks.  Two "chain" waves keep the state block in
+//      MFMA accumulators and carry h -> K h -> X -> E X -> h entirely in registers
+//      (the only exchange per chunk is the sum of their two halves of K h, through
+//      LDS); two "output" waves compute O one chunk behind.  See the comment at the
+//      kernel.  Columns of h evolve independently, so a 128-wide state splits into 8
+//      workgroups; those of the value heads of one key head are mapped onto one XCD
+//      so they share its operands through one L2.
 // Precision: fp32-derived operands (h, X, T, E, MT, and fp32 activations) enter
 // MFMA as bf16 hi + lo; a product takes hi*hi + hi*lo + lo*hi, about 2^-16
 // relative, which keeps states within 1e-4 of the fp64 recurrence.
@@ -61,6 +64,25 @@ int64_t max_chunks(int n, int64_t T) { return T / kC + n; }
 __host__ __device__ constexpr size_t unit_bytes(int D) { return a256((size_t)4 * D * kC + (size_t)4 * kC * kC + 256); }
 // Element offset of lane `lane`'s 8 values of fragment (tile, ks) with nks k-steps.
 __host__ __device__ constexpr int frag_off(int tile, int ks, int nks, int lane) { return ((tile * nks + ks) * 64 + lane) * 8; }
+
+// Row order of the spine's operands.  A 16x16 MFMA result leaves lane (n, g)
+// holding rows 4g .. 4g + 3 of column n; the B operand of a 16x16x32 product wants
+// lane (n, g) to hold k-indices 8g .. 8g + 7.  If the rows of result tile t are the
+// matrix rows
+//      row_of(t, m) = 32 (t / 2) + 8 (m / 4) + 4 (t % 2) + m % 4     (m = 0..15),
+// then result tiles 2s and 2s + 1 give lane (n, g) exactly the rows
+// 32 s + 8 g .. 32 s + 8 g + 7 in order: they ARE the B operand of k-step s of the
+// next product, with no data movement.  The spine therefore takes the rows of every
+// A operand in this order -- the token rows of K and Q (loaded so) and the rows of E
+// (d_k) and MT (tokens), stored so by the prep -- while k-indices stay natural.
+__host__ __device__ constexpr int row_of(int t, int m) { return 32 * (t >> 1) + 8 * (m >> 2) + 4 * (t & 1) + (m & 3); }
+// Element offset of matrix entry (row, col) of a 64-column E or MT plane in that
+// order: tile t and operand row m with row_of(t, m) == row, k-step col / 32, lane
+// m + 16 ((col % 32) / 8), element col % 8.
+__host__ __device__ constexpr int pfrag_off(int row, int col) {
+  return frag_off(2 * (row >> 5) + ((row >> 2) & 1), col >> 5, 2, 4 * ((row >> 3) & 3) + (row & 3) + 16 * ((col >> 3) & 3)) +
+         (col & 7);
+}
 
 struct Tables {
   int32_t *seq_chunk0;   // [n+1] first chunk of each sequence
@@ -460,9 +482,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   }
   __syncthreads();
   // The lane's results below are X[r0 + lr][16 wave + 4 lg + r], r = 0..3 (X = MT or E,
-  // r0 the tile's first row): k-offset 16 (wave & 1) + 4 lg + r within k-step wave / 2,
-  // i.e. fragment lane fl, elements fe .. fe + 3.
-  const int fl = lr + 16 * (2 * (wave & 1) + (lg >> 1)), fe = 4 * (lg & 1);
+  // r0 the tile's first row): four consecutive columns, one 8-byte word of the
+  // spine's fragment order (pfrag_off).
   // MT^T[j][t] = sum_s T[s][j] M[t][s]; lane holds column t, rows j..j+3 -> MT[t][j..j+3]
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
@@ -474,7 +495,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       acc = mma<true, true>(acc, th[ks], tl[ks], mh, ml);
     }
     const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    const int fo = frag_off(tt, wave >> 1, 2, fl) + fe;
+    const int fo = pfrag_off(16 * tt + lr, 16 * wave + 4 * lg);
     store_split4(MT_hi + fo, MT_lo + fo, v);
   }
   // E^T[j][i] = sum_s D_s T[s][j] K[s][i]; lane holds column i, rows j..j+3 -> E[i][j..j+3]
@@ -489,41 +510,41 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
     }
     const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    const int fo = frag_off(tix, wave >> 1, 2, fl) + fe;
+    const int fo = pfrag_off(16 * tix + lr, 16 * wave + 4 * lg);
     store_split4(E_hi + fo, E_lo + fo, v);
   }
 }
 
 // ---- 3. the serial pass over chunks -------------------------------------------
-// 512 threads per (sequence, value head, 32-column block of d_v).  Columns of h
-// evolve independently, so a d_v-wide state splits over d_v / 32 workgroups.
-//   waves 0-1 ("K-row waves"): token rows 32 w .. +31.  Stage 1: P^T = h^T K^T,
-//       X = V - Gam P -> LDS.  Stage 2: fetch the next chunk's K rows, V, Gam.
-//   waves 2-3 ("Q-row waves"): token rows 32 (w - 2) .. +31.  Stage 1: R^T = h^T Q^T,
-//       then fetch the next chunk's Q rows and Gam.  Stage 2: O^T = Gam R^T +
-//       X^T MT^T, stored; then fetch the next chunk's MT.
-//   waves 4-7 ("owners"): state rows 32 (w - 4) .. +31 of the block live in MFMA
-//       accumulators.  Stage 1: fetch the next chunk's E (double-buffered).
-//       Stage 2: h <- Gam_63 h + E X, copied as bf16 hi/lo h^T to LDS.
-// One barrier after each stage; each role runs its own loop, with the same two
-// barriers per chunk, so the compiler tracks each role's loads, waits and
-// registers on their own.  Each wave loads exactly the operands it consumes (84 KiB
-// per chunk and workgroup at d = 128, nothing read twice), all as 16-byte
-// accesses: the per-CU vector-memory path spends about as long on a 2-byte load
-// instruction as on a 16-byte one, and its throughput sets the pace of a chunk.
-// Loads for chunk c+1 go out right after the last use of the registers they fill
-// and land while chunk c computes.
-//
-// Column order: inside the workgroup, state column j (0..31) of the block sits at
-// position jj = 16 (j & 1) + j / 2, so MFMA column tile ct holds the columns of
-// parity ct.  The products with h are taken transposed (h^T times rows), and a
-// lane then holds, for one token row, positions 16 ct + 4 lg + r (r = 0..3,
-// ct = 0..1), which are the 8 consecutive columns 8 lg .. 8 lg + 7: one 16-byte V
-// load and one 16-byte O store per token tile.
-constexpr int kCols = 32;  // state columns per workgroup
+// One workgroup of 8 waves per (sequence, value head, 16-column block of d_v);
+// columns of h evolve independently, so a d_v-wide state splits over d_v / 16
+// workgroups.
+//   waves 0 .. D/32 - 1 ("chain"): wave w keeps d_k rows [32 w, 32 w + 32) of the
+//     state block h (fp32) in MFMA accumulators -- one k-step of every product with
+//     h.  Per chunk:
+//       P_w = K[:, rows of w] h_w          partial K h for all 64 tokens (8 MFMAs)
+//       -- barrier 1 --
+//       wave w sums the partials of its own token tiles (fixed order), forms
+//       X = V - Gam P for them and writes them, split bf16 hi/lo, as its part of
+//       the B operand of the token k-steps in LDS
+//       -- barrier 2 --
+//       h_w <- Gam_63 h_w + E[rows of w, :] X   (X from LDS; 12 MFMAs)
+//     With the operand row order of row_of(), each product's result tiles are lane
+//     by lane the B operand of the next product: h, P and X only change precision
+//     (bf16 hi/lo split), never lanes, and the work of forming X is split over the
+//     chain waves instead of repeated in each.
+//   waves 4 .. 7 ("output"): token tile w - 4; after barrier 1 of chunk c,
+//     R = Gam (Q h) with h from LDS; after barrier 2, O = scale (R + MT X), stored.
+// LDS: the partial products, h for the output waves (2 slots) and X (2 slots).
+// Every wave loads exactly the operands it consumes (16-byte accesses but for V)
+// through buffer descriptors whose extent ends at the chunk's last row, so rows
+// past it read as zero and stores there are dropped; loads for a later chunk go out
+// right after the last use of the registers they fill and stay raw until used.
+constexpr int kCB = 16;  // state columns of one column tile
+// 32-column workgroups once 16-column ones would exceed twice this many
+constexpr int64_t kSpineWideMinBlocks = 256;
 
-// K or Q row fragments (bf16: one 16-byte word, fp32: two) and V words, kept raw
-// until used.
+// K or Q row fragments (bf16: one 16-byte word, fp32: two) kept raw until used.
 template <typename TY>
 struct Raw8;
 template <>
@@ -540,50 +561,86 @@ __device__ __forceinline__ void load8(Raw8<float> &r, const float *p) {
   r.w1 = reinterpret_cast<const uint4 *>(p)[1];
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
-// the 8 values as floats
-__device__ __forceinline__ void unpack8(const Raw8<bf16> &r, float v[8]) {
-  const bf16x8 b = as_bf16x8(r.w);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
-}
-__device__ __forceinline__ void unpack8(const Raw8<float> &r, float v[8]) {
-  const float4 a = __builtin_bit_cast(float4, r.w0), b = __builtin_bit_cast(float4, r.w1);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
 // as an MFMA operand: bf16 is exact (lo unused), fp32 splits into hi + lo
 __device__ __forceinline__ void split8(const Raw8<bf16> &r, bf16x8 &hi, bf16x8 &lo) {
   hi = as_bf16x8(r.w);
   lo = hi;
 }
 __device__ __forceinline__ void split8(const Raw8<float> &r, bf16x8 &hi, bf16x8 &lo) {
-  float v[8];
-  unpack8(r, v);
+  const floatx4 a = __builtin_bit_cast(floatx4, r.w0), b = __builtin_bit_cast(floatx4, r.w1);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16 h, l;
-    split_bf16(v[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
+  for (int e = 0; e < 4; ++e) {
+    bf16 h0, l0, h1, l1;
+    split_bf16(a[e], h0, l0);
+    split_bf16(b[e], h1, l1);
+    hi[e] = h0;
+    lo[e] = l0;
+    hi[4 + e] = h1;
+    lo[4 + e] = l1;
   }
 }
+// One activation kept raw: bf16 as its 16 bits, fp32 as is.
+template <typename TY>
+struct RawS;
+template <>
+struct RawS<bf16> {
+  uint16_t v;
+};
+template <>
+struct RawS<float> {
+  float v;
+};
+__device__ __forceinline__ void loads(RawS<bf16> &r, const bf16 *p) { r.v = *reinterpret_cast<const uint16_t *>(p); }
+__device__ __forceinline__ void loads(RawS<float> &r, const float *p) { r.v = *p; }
+__device__ __forceinline__ float unpack(const RawS<bf16> &r) { return __builtin_bit_cast(float, (uint32_t)r.v << 16); }
+__device__ __forceinline__ float unpack(const RawS<float> &r) { return r.v; }
 
-__device__ __forceinline__ void store8(float *p, const float v[8]) {
-  reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-  reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+// Buffer accesses: a descriptor (base address, extent in bytes) in scalar registers
+// and a 32-bit per-lane byte offset.  Reads at or past the extent return zero and
+// writes there are dropped, so rows past a chunk's end need no clamp and no branch.
+// Every offset that the range check must see goes into the per-lane offset.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, int64_t bytes) {
+  const int n = (int)(bytes < 0 ? 0 : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
 }
-__device__ __forceinline__ void store8(bf16 *p, const float v[8]) {
-  bf16x8 b;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = (bf16)v[e];
-  *reinterpret_cast<bf16x8 *>(p) = b;
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bload(Raw8<bf16> &v, Rsrc r, uint32_t off) { v.w = bload16(r, off); }
+__device__ __forceinline__ void bload(Raw8<float> &v, Rsrc r, uint32_t off) {
+  v.w0 = bload16(r, off);
+  v.w1 = bload16(r, off + 16);
+}
+__device__ __forceinline__ void bload(RawS<bf16> &v, Rsrc r, uint32_t off) {
+  v.v = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bload(RawS<float> &v, Rsrc r, uint32_t off) {
+  v.v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void store_raw(bf16 *p, const Raw8<bf16> &v) { *reinterpret_cast<uint4 *>(p) = v.w; }
+__device__ __forceinline__ void store_raw(float *p, const Raw8<float> &v) {
+  reinterpret_cast<uint4 *>(p)[0] = v.w0;
+  reinterpret_cast<uint4 *>(p)[1] = v.w1;
+}
+__device__ __forceinline__ floatx4 bloadf4(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void bstore(Rsrc r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void bstore(Rsrc r, uint32_t off, bf16 v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, (int)off, 0, 0);
 }
 
-template <int D, typename TY, typename TO>
+template <int D, int NC, typename TY, typename TO>
 __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, const char *units) {
   constexpr bool SP = std::is_same<TY, float>::value;
-  constexpr int KS = D / 32;
-  constexpr int NRT = D / 16;
-  constexpr int NCB = D / kCols;
+  constexpr int KS = D / 32;        // k-steps over d_k = chain waves
+  constexpr int CB = kCB * NC;      // state columns per workgroup (NC tiles of 16)
+  constexpr int NCB = D / CB;       // column blocks per head
+  constexpr int TPW = 4 / KS;       // token tiles whose X a chain wave forms
+  constexpr int NT = SP ? 3 : 2;    // terms of a product with h: hi hi, hi lo (, lo hi)
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   // Consecutive workgroups are dispatched round-robin over the 8 XCDs; within
   // each group of 8 * G * NCB, remap so that one XCD receives the NCB column blocks
@@ -606,277 +663,313 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   const int g = h / G;
   const int lane = threadIdx.x % kWave, lr = lane % 16, lg = lane / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int rblk = wave & 1;  // row waves: token rows 32 rblk .. +31
-  const int ob = wave - 4;    // owners: state tiles 2 ob, 2 ob + 1
-  const int vcol = 2 * Hk * D + h * D + kCols * cb;
 
-  __shared__ __align__(16) bf16 s_hT[2][kCols][D + 8];  // state block h^T [jj][i], hi/lo
-  __shared__ __align__(16) bf16 s_XT[2][kCols][kLP];    // X^T [jj][t], hi/lo
+  // One slot each: partials are written before barrier 1 and read before barrier 2;
+  // h is written before barrier 1 and read (by the output waves) before barrier 2;
+  // X is written between the barriers and read before the next chunk's barrier 1.
+  __shared__ floatx4 s_P[KS][4][NC][kWave];    // partial K h: chain wave, token tile, column tile
+  __shared__ bf16x8 s_H[KS][2][NC][kWave];     // h as B operands: k-step, hi/lo, column tile
+  __shared__ uint2 s_X[2][2][NC][kWave][2];    // X as B operands: token k-step, hi/lo, column tile, lane, tile parity
+  // V and Gam of the next chunk, from the output waves (each loads its token tile's
+  // V rows with one 16-byte access per lane), for the chain waves; written before
+  // barrier 1, read before barrier 2.  V rows in operand-row order m of the tile.
+  __shared__ __align__(16) TY s_V[4][16][CB];
+  __shared__ floatx4 s_G[4][kWave];           // Gam of token row_of(tt, 4 lg + r)
 
   const TY *y = static_cast<const TY *>(p.y);
-  TO *o = static_cast<TO *>(p.o);
-  const size_t ostride = (size_t)Hv * D;
-  // the sequence's state: fp32, or binary16 widened here and narrowed at the end
-  const size_t hoff = (size_t)h * D * D + kCols * cb;
-  gptr<float> hs = to_global(static_cast<float *>(p.h_state[seq])) + hoff;
-  gptr<_Float16> hs16 = to_global(static_cast<_Float16 *>(p.h_state[seq])) + hoff;
   auto unit_of = [&](int c) { return units + ((size_t)(c_first + c) * Hv + h) * unit_bytes(D); };
   auto gam_of = [&](int c) {
     return reinterpret_cast<const float *>(reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC + 2 * kC * kC);
   };
   auto chunk_t0 = [&](int c) { return seq_t0 + kC * c; };
   auto chunk_len = [&](int c) { return min(kC, seq_len - kC * c); };
-  // row waves: token row of tile rt in chunk c, clamped into the chunk (rows past
-  // its end only meet zero columns of E and MT, and are not stored)
-  auto row_of = [&](int c, int rt) { return chunk_t0(c) + min(32 * rblk + 16 * rt + lr, chunk_len(c) - 1); };
+  // Descriptor of the y rows of token tile tt of chunk c (row order row_of): base at
+  // the tile's first row 32 (tt / 2) + 4 (tt % 2), extent up to the chunk's end, so
+  // rows past it read as zero.
+  auto tile_rows = [&](int c, int tt) {
+    const int r0 = 32 * (tt >> 1) + 4 * (tt & 1);
+    return make_rsrc(y + (size_t)(chunk_t0(c) + r0) * CD, (int64_t)(chunk_len(c) - r0) * CD * (int64_t)sizeof(TY));
+  };
+  constexpr uint32_t kGamOff = 2 * (2 * D * kC + 2 * kC * kC);  // byte offset of Gam in a unit
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
 
-  // ---- row waves: shared pieces ----
-  Raw8<TY> rows[2][KS];
-  float gt[2];
-  auto fetch_rows = [&](int c, int col) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const TY *ar = y + (size_t)row_of(c, rt) * CD + col + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) load8(rows[rt][ks], ar + 32 * ks);
-    }
-  };
-  auto fetch_gt = [&](int c) {
-    const float *Gam = gam_of(c);
-    gt[0] = Gam[32 * rblk + lr];
-    gt[1] = Gam[32 * rblk + 16 + lr];
-  };
-  // P^T or R^T = h^T (rows)^T: acc[rt][ct][0] takes the h_hi terms, [1] the rest;
-  // lane holds position 16 ct + 4 lg + r of token 32 rblk + 16 rt + lr
-  auto row_products = [&](floatx4 (&acc)[2][2][2]) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) acc[rt][ct][0] = acc[rt][ct][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 bh[2], bl[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        bh[ct] = *reinterpret_cast<const bf16x8 *>(&s_hT[0][16 * ct + lr][32 * ks + 8 * lg]);
-        bl[ct] = *reinterpret_cast<const bf16x8 *>(&s_hT[1][16 * ct + lr][32 * ks + 8 * lg]);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        bf16x8 ah, al;
-        split8(rows[rt][ks], ah, al);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          acc[rt][ct][0] = mfma16(bh[ct], ah, acc[rt][ct][0]);
-          acc[rt][ct][1] = mfma16(bl[ct], ah, acc[rt][ct][1]);
-          if (SP) acc[rt][ct][1] = mfma16(bh[ct], al, acc[rt][ct][1]);
-        }
-      }
-    }
-  };
-  auto load_xt = [&](bf16x8 (&xh)[2][2], bf16x8 (&xl)[2][2]) {
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        xh[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[0][16 * ct + lr][32 * ks + 8 * lg]);
-        xl[ct][ks] = *reinterpret_cast<const bf16x8 *>(&s_XT[1][16 * ct + lr][32 * ks + 8 * lg]);
-      }
-  };
-
-  if (wave < 2) {
-    // ---------------- K-row waves ----------------
-    const int kcol = (Hk + g) * D;
-    Raw8<TY> vv[2];
-    auto fetch_v = [&](int c) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) load8(vv[rt], y + (size_t)row_of(c, rt) * CD + vcol + 8 * lg);
-    };
-    fetch_rows(0, kcol);
-    fetch_v(0);
-    fetch_gt(0);
-    __syncthreads();
+  if (wave < 4) {
+    if (wave >= KS) {  // D < 128: fewer chain waves; keep the barrier count
 #pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-      floatx4 acc[2][2][2];
-      row_products(acc);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int t = 32 * rblk + 16 * rt + lr;
-        float v[8];
-        unpack8(vv[rt], v);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float X = v[2 * r + ct] - gt[rt] * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
-            bf16 hi, lo;
-            split_bf16(X, hi, lo);
-            s_XT[0][16 * ct + 4 * lg + r][t] = hi;
-            s_XT[1][16 * ct + 4 * lg + r][t] = lo;
-          }
+      for (int c = 0; c < nch; ++c) {
+        __syncthreads();
+        __syncthreads();
       }
-      __syncthreads();
-      // no stage-2 work: fetch the next chunk (past the end: the last one again, unused)
-      const int cn = min(c + 1, nch - 1);
-      fetch_rows(cn, kcol);
-      fetch_v(cn);
-      fetch_gt(cn);
-      __syncthreads();
+      return;
     }
-  } else if (wave < 4) {
-    // ---------------- Q-row waves ----------------
-    const int qcol = g * D;
-    uint4 mt[2][4];  // MT fragments of the two token tiles: hi k0, hi k1, lo k0, lo k1
-    auto fetch_mt = [&](int c) {
-      const bf16 *MT = reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC;
+    // ---------------- chain waves ----------------
+    const int cw = wave;
+    const int kcol = (Hk + g) * D + 32 * cw;  // this wave's d_k columns of K
+    // the sequence's state: fp32, or binary16 widened here and narrowed at the end;
+    // result tile (i, ct) of this wave holds d_k rows row_of(2 cw + i, 4 lg + r) of
+    // column 16 ct + lr of the block
+    const size_t hoff = (size_t)h * D * D + CB * cb + lr;
+    gptr<float> hs = to_global(static_cast<float *>(p.h_state[seq])) + hoff;
+    gptr<_Float16> hs16 = to_global(static_cast<_Float16 *>(p.h_state[seq])) + hoff;
+    // all of the block's state loads first (one branch on the stored width)
+    floatx4 hacc[2][NC];
+    if (p.state_f16) {
+      _Float16 raw[2][NC][4];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          mt[rt][ks] = *reinterpret_cast<const uint4 *>(MT + frag_off(2 * rblk + rt, ks, 2, lane));
-          mt[rt][2 + ks] = *reinterpret_cast<const uint4 *>(MT + kC * kC + frag_off(2 * rblk + rt, ks, 2, lane));
-        }
-    };
-    fetch_rows(0, qcol);
-    fetch_gt(0);
-    fetch_mt(0);
-    __syncthreads();
-#pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-      const int L = chunk_len(c), cn = min(c + 1, nch - 1);
-      floatx4 acc[2][2][2], Ot[2][2];
-      row_products(acc);
+        for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+          for (int r = 0; r < 4; ++r) raw[i][ct][r] = hs16[(size_t)row_of(2 * cw + i, 4 * lg + r) * D + 16 * ct];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Ot[rt][ct][r] = gt[rt] * (acc[rt][ct][0][r] + acc[rt][ct][1][r]);
-      // this chunk's Q rows and Gam are consumed
-      fetch_rows(cn, qcol);
-      fetch_gt(cn);
-      __syncthreads();
-      bf16x8 xh[2][2], xl[2][2];
-      load_xt(xh, xl);
-      // the four output tiles are independent accumulation chains: innermost, so
-      // that consecutive MFMAs never wait for each other's results
+        for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+          for (int r = 0; r < 4; ++r) hacc[i][ct][r] = (float)raw[i][ct][r];
+    } else {
 #pragma unroll
-        for (int term = 0; term < 3; ++term)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
+        for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              const bf16x8 a = term == 1 ? xl[ct][ks] : xh[ct][ks];
-              const bf16x8 m = as_bf16x8(term == 2 ? mt[rt][2 + ks] : mt[rt][ks]);
-              Ot[rt][ct] = mfma16(a, m, Ot[rt][ct]);
-            }
-      fetch_mt(cn);  // issued while the O products are in flight
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int t = 32 * rblk + 16 * rt + lr;
-        float v[8];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[2 * r + ct] = p.scale * Ot[rt][ct][r];
-        if (t < L) store8(o + (size_t)(chunk_t0(c) + t) * ostride + (size_t)h * D + kCols * cb + 8 * lg, v);
-      }
-      __syncthreads();
+          for (int r = 0; r < 4; ++r) hacc[i][ct][r] = hs[(size_t)row_of(2 * cw + i, 4 * lg + r) * D + 16 * ct];
     }
-  } else if (2 * ob < NRT) {
-    // ---------------- owners ----------------
-    uint4 ef[2][2][4];  // E fragments [parity][tile][hi k0, hi k1, lo k0, lo k1]
-    float gcv[2];       // Gam_63 of the chunks of parity 0 / 1
-    auto fetch_e = [&](int par, int c) {
-      const bf16 *E = reinterpret_cast<const bf16 *>(unit_of(c));
+    Raw8<TY> kf[4];               // K rows of token tile tt (row order row_of), this wave's k-step
+    uint4 ef[2][2][2];            // E fragments: result tile, token k-step, hi / lo
+    float gC = 0.0f;              // Gam_63
+    // per-lane byte offsets, the same for every chunk, within a token tile's rows
+    // (row_of(tt, m) = first row of tt + 8 (m / 4) + m % 4)
+    const uint32_t koff = ((8 * (lr >> 2) + (lr & 3)) * CD + kcol + 8 * lg) * (uint32_t)sizeof(TY);
+    auto fetch_k = [&](int c) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-          ef[par][t][qq] = *reinterpret_cast<const uint4 *>(E + frag_off(2 * ob + t, qq, 2, lane));
-          ef[par][t][2 + qq] = *reinterpret_cast<const uint4 *>(E + D * kC + frag_off(2 * ob + t, qq, 2, lane));
-        }
-      gcv[par] = gam_of(c)[kC - 1];
+      for (int tt = 0; tt < 4; ++tt) bload(kf[tt], tile_rows(c, tt), koff);
     };
-    // lane holds h[16 tile + 4 lg + r][column 2 lr + ct] (position 16 ct + lr)
-    floatx4 hacc[2][2];
-    fetch_e(0, 0);
+    auto fetch_e = [&](int c) {
+      const Rsrc ru = make_rsrc(unit_of(c), unit_bytes(D));
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const size_t e = (size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct;
-          hacc[t][ct][r] = p.state_f16 ? (float)hs16[e] : hs[e];
-        }
-        const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
-        store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
-                     &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
-      }
-    __syncthreads();
-    // PAR = c & 1 as a compile-time constant: the two E buffers are fixed registers
-    auto owner_chunk = [&](int c, auto par) {
+          for (int hl = 0; hl < 2; ++hl)
+            ef[i][s][hl] = bload16(ru, 2 * (uint32_t)(hl * D * kC + frag_off(2 * cw + i, s, 2, lane)));
+      gC = gam_of(c)[kC - 1];
+    };
+    fetch_k(0);
+    fetch_e(0);
+    auto chain_chunk = [&](int c, auto par) {
       constexpr int PAR = decltype(par)::value;
-      fetch_e(PAR ^ 1, min(c + 1, nch - 1));  // next chunk's E, during stage 1
-      __syncthreads();
-      bf16x8 xh[2][2], xl[2][2];
-      load_xt(xh, xl);
-      const float gC = gcv[PAR];
+      const int cn = min(c + 1, nch - 1);  // past the end: the last chunk again, unused
+      // h as the B operand (hi, lo) of this wave's k-step; to LDS for the output waves
+      bf16x8 hb[NC][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int ct = 0; ct < NC; ++ct) {
+        const Split2 a0 = split_bf16_2(hacc[0][ct][0], hacc[0][ct][1]), a1 = split_bf16_2(hacc[0][ct][2], hacc[0][ct][3]);
+        const Split2 b0 = split_bf16_2(hacc[1][ct][0], hacc[1][ct][1]), b1 = split_bf16_2(hacc[1][ct][2], hacc[1][ct][3]);
+        hb[ct][0] = __builtin_bit_cast(bf16x8, uint4{a0.hi, a1.hi, b0.hi, b1.hi});
+        hb[ct][1] = __builtin_bit_cast(bf16x8, uint4{a0.lo, a1.lo, b0.lo, b1.lo});
+        s_H[cw][0][ct][lane] = hb[ct][0];
+        s_H[cw][1][ct][lane] = hb[ct][1];
+      }
+      // partial P = K h over this wave's rows; the token and column tiles are
+      // independent accumulation chains, innermost
+      floatx4 pp[4][NC];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) hacc[t][ct] *= gC;
-      // four independent accumulation chains, innermost (see the O products)
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ct = 0; ct < NC; ++ct) pp[tt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      {
+        bf16x8 kh[4], kl[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) split8(kf[tt], kh[tt], kl[tt]);
+#pragma unroll
+        for (int term = 0; term < NT; ++term)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ct = 0; ct < NC; ++ct)
+              pp[tt][ct] = mfma16(term == 2 ? kl[tt] : kh[tt], term == 1 ? hb[ct][1] : hb[ct][0], pp[tt][ct]);
+      }
+      if (KS > 1) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < NC; ++ct) s_P[cw][tt][ct][lane] = pp[tt][ct];
+      }
+      fetch_k(cn);
+      __syncthreads();  // barrier 1
+      // X of the own token tiles: partials summed in wave order (the own one read
+      // back too: picking it out of pp by the wave-dependent tile index would put pp
+      // in scratch memory), then V - Gam P, split into this wave's half of the token
+      // k-step's B operand
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int tt = TPW * cw + j;
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+          floatx4 P;
+          if (KS == 1) {
+            P = pp[j][ct];
+          } else {
+            P = s_P[0][tt][ct][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < KS; ++w2) P += s_P[w2][tt][ct][lane];
+          }
+          const floatx4 gam = s_G[tt][lane];
+          float X[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X[r] = ld(&s_V[tt][4 * lg + r][0], 16 * ct + lr) - gam[r] * P[r];
+          const Split2 x01 = split_bf16_2(X[0], X[1]), x23 = split_bf16_2(X[2], X[3]);
+          s_X[tt >> 1][0][ct][lane][tt & 1] = uint2{x01.hi, x23.hi};
+          s_X[tt >> 1][1][ct][lane][tt & 1] = uint2{x01.lo, x23.lo};
+        }
+      }
+      __syncthreads();  // barrier 2
+      bf16x8 xb[2][2][NC];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+          for (int ct = 0; ct < NC; ++ct) xb[s][hl][ct] = *reinterpret_cast<const bf16x8 *>(&s_X[s][hl][ct][lane][0]);
+      // h <- Gam_63 h + E X: hi hi, hi lo, lo hi
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) hacc[i][ct] *= gC;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int term = 0; term < 3; ++term)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              const bf16x8 e = as_bf16x8(term == 2 ? ef[PAR][t][2 + ks] : ef[PAR][t][ks]);
-              hacc[t][ct] = mfma16(e, term == 1 ? xl[ct][ks] : xh[ct][ks], hacc[t][ct]);
-            }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const float v[4] = {hacc[t][ct][0], hacc[t][ct][1], hacc[t][ct][2], hacc[t][ct][3]};
-          store_split4(&s_hT[0][16 * ct + lr][16 * (2 * ob + t) + 4 * lg],
-                       &s_hT[1][16 * ct + lr][16 * (2 * ob + t) + 4 * lg], v);
-        }
-      __syncthreads();
+            for (int ct = 0; ct < NC; ++ct)
+              hacc[i][ct] = mfma16(as_bf16x8(ef[i][s][term == 2 ? 1 : 0]), term == 1 ? xb[s][1][ct] : xb[s][0][ct],
+                                   hacc[i][ct]);
+      fetch_e(cn);
     };
 #pragma unroll 1
     for (int c = 0; c < nch; c += 2) {
-      owner_chunk(c, std::integral_constant<int, 0>());
+      chain_chunk(c, P0());
       if (c + 1 >= nch) break;
-      owner_chunk(c + 1, std::integral_constant<int, 1>());
+      chain_chunk(c + 1, P1());
     }
+    if (p.state_f16) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < NC; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const size_t e = (size_t)(16 * (2 * ob + t) + 4 * lg + r) * D + 2 * lr + ct;
-          if (p.state_f16)
-            hs16[e] = (_Float16)hacc[t][ct][r];
-          else
-            hs[e] = hacc[t][ct][r];
-        }
+          for (int r = 0; r < 4; ++r)
+            hs16[(size_t)row_of(2 * cw + i, 4 * lg + r) * D + 16 * ct] = (_Float16)hacc[i][ct][r];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hs[(size_t)row_of(2 * cw + i, 4 * lg + r) * D + 16 * ct] = hacc[i][ct][r];
+    }
   } else {
-    // waves without state rows (d_k < 128): keep the barrier count
-    __syncthreads();
+    // ---------------- output waves ----------------
+    const int tt = wave - 4;  // token tile
+    const int qcol = g * D;
+    TO *o = static_cast<TO *>(p.o);
+    const size_t ostride = (size_t)Hv * D;
+    const int ocol = h * D + CB * cb + lr;
+    const uint32_t ooff = (uint32_t)((8 * lg * ostride + ocol) * sizeof(TO));
+    const uint32_t qoff = ((8 * (lr >> 2) + (lr & 3)) * CD + qcol + 8 * lg) * (uint32_t)sizeof(TY);
+    Raw8<TY> qf[2][KS];   // Q rows of the tile (row order row_of), all k-steps; chunk parity
+    uint4 mf[2][2][2];    // MT fragments: chunk parity, token k-step, hi / lo
+    floatx4 go[2];        // Gam of the tile's tokens; chunk parity
+    Raw8<TY> vr[2];       // V of the tile for the chain waves: operand row vm, 8 columns from vc
+    // V of the tile's 16 rows x CB columns, 8 columns per lane (lanes past 2 CB
+    // rows' worth -- 16-column blocks -- repeat the first half: same data)
+    constexpr int LPR = CB / 8;  // lanes per row
+    const int vm = (lane / LPR) & 15, vc = 8 * (lane % LPR);
+    const uint32_t vof = ((8 * (vm >> 2) + (vm & 3)) * CD + 2 * Hk * D + h * D + CB * cb + vc) * (uint32_t)sizeof(TY);
+    auto fetch_q = [&](auto par, int c) {
+      constexpr int PAR = decltype(par)::value;
+      const Rsrc rt = tile_rows(c, tt);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) bload(qf[PAR][s], rt, qoff + 32 * s * (uint32_t)sizeof(TY));
+      bload(vr[PAR], rt, vof);
+      go[PAR] = bloadf4(make_rsrc(unit_of(c), unit_bytes(D)), kGamOff + 4 * (uint32_t)row_of(tt, 4 * lg));
+    };
+    // the chunk's V (in the activation dtype) and Gam to LDS for the chain waves
+    auto put_vg = [&](auto par) {
+      constexpr int PAR = decltype(par)::value;
+      store_raw(&s_V[tt][vm][vc], vr[PAR]);
+      s_G[tt][lane] = go[PAR];
+    };
+    auto fetch_mt = [&](auto par, int c) {
+      constexpr int PAR = decltype(par)::value;
+      const Rsrc ru = make_rsrc(unit_of(c), unit_bytes(D));
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl)
+          mf[PAR][s][hl] = bload16(ru, 2 * (uint32_t)(2 * D * kC + hl * kC * kC + frag_off(tt, s, 2, lane)));
+    };
+    auto out_chunk = [&](int c, auto par) {
+      constexpr int PAR = decltype(par)::value;
+      __syncthreads();  // barrier 1: h of chunk c is in LDS
+      floatx4 O[NC];
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) O[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        bf16x8 qh, ql;
+        split8(qf[PAR][s], qh, ql);
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+          const bf16x8 hh = s_H[s][0][ct][lane], hl = s_H[s][1][ct][lane];
+          O[ct] = mfma16(qh, hh, O[ct]);
+          O[ct] = mfma16(qh, hl, O[ct]);
+          if (SP) O[ct] = mfma16(ql, hh, O[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) O[ct] *= go[PAR];
+      fetch_q(par, min(c + 2, nch - 1));  // this chunk's Q and Gam are consumed
+      __syncthreads();  // barrier 2: X of chunk c is in LDS
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) {
+          const bf16x8 xh = *reinterpret_cast<const bf16x8 *>(&s_X[s][0][ct][lane][0]);
+          const bf16x8 xl = *reinterpret_cast<const bf16x8 *>(&s_X[s][1][ct][lane][0]);
+          O[ct] = mfma16(as_bf16x8(mf[PAR][s][0]), xh, O[ct]);
+          O[ct] = mfma16(as_bf16x8(mf[PAR][s][0]), xl, O[ct]);
+          O[ct] = mfma16(as_bf16x8(mf[PAR][s][1]), xh, O[ct]);
+        }
+      // stores through the tile's descriptor over o: rows past the chunk's end are dropped
+      const int r0 = 32 * (tt >> 1) + 4 * (tt & 1);
+      const Rsrc ro = make_rsrc(o + (size_t)(chunk_t0(c) + r0) * ostride,
+                                (int64_t)(chunk_len(c) - r0) * (int64_t)ostride * (int64_t)sizeof(TO));
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          bstore(ro, ooff + (uint32_t)((r * ostride + 16 * ct) * sizeof(TO)), (TO)(p.scale * O[ct][r]));
+      fetch_mt(par, min(c + 2, nch - 1));
+      // next chunk's V and Gam for the chain waves (read after barrier 1; the chain
+      // waves finished reading this chunk's before barrier 2)
+      if (PAR == 0) put_vg(P1()); else put_vg(P0());
+    };
+    fetch_q(P0(), 0);
+    fetch_mt(P0(), 0);
+    fetch_q(P1(), min(1, nch - 1));
+    fetch_mt(P1(), min(1, nch - 1));
+    put_vg(P0());
 #pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-      __syncthreads();
-      __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+      out_chunk(c, P0());
+      if (c + 1 >= nch) break;
+      out_chunk(c + 1, P1());
     }
   }
 }
@@ -898,8 +991,16 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
   hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hv)), dim3(256), 0, stream, p, tb, units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((spine_kernel<D, TY, TO>), dim3((unsigned)(p.n * p.geo.Hv * (D / kCols))), dim3(512), 0,
-                     stream, p, tb, static_cast<const char *>(units));
+  // 16-column blocks while that is what it takes to give every CU a workgroup
+  // (the chunk time of a block is bound by the operands it loads, the same for 16 or
+  // 32 columns); 32-column blocks, half the operand traffic, for larger batches.
+  const int64_t wg16 = (int64_t)p.n * p.geo.Hv * (D / kCB);
+  if (D >= 32 && wg16 > 2 * kSpineWideMinBlocks)
+    hipLaunchKernelGGL((spine_kernel<D, 2, TY, TO>), dim3((unsigned)(wg16 / 2)), dim3(512), 0, stream, p, tb,
+                       static_cast<const char *>(units));
+  else
+    hipLaunchKernelGGL((spine_kernel<D, 1, TY, TO>), dim3((unsigned)wg16), dim3(512), 0, stream, p, tb,
+                       static_cast<const char *>(units));
   return hipGetLastError();
 }
 
