@@ -43,20 +43,21 @@ DECODE_LAYERS = 4                       # disjoint state sets the decode launche
 VERIFY_SETS = 2                         # state sets the verify/commit alternate between
 
 
-# HBM traffic of one decode launch (recurrent_kernel<128,2,1>), from two rocprofv3
-# counter runs of `bench.py --steps 1 --warmup 0 --no-cpu-baseline` (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch, mean of the 100 decode dispatches), each scaled by
-# what the same counter reads for one 1 GiB device copy (`bench.py --copy-calib`:
-# FETCH_SIZE 524302.1 KiB, WRITE_SIZE 1048576.0 KiB per copy).  The figures hold for
-# the kernel sources they were taken on only (SHA-256 over the files below); for any
-# other source the traffic is reported as unknown.
+# HBM traffic of one decode launch (recurrent_kernel<128,2,1>) in the bench step --
+# cache-cold, the 100 launches cycling over DECODE_LAYERS state sets -- from two
+# rocprofv3 counter runs of `bench.py --steps 1 --warmup 0 --no-cpu-baseline`
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean of the step's decode dispatches),
+# each scaled by what the same counter reads for one 1 GiB device copy (`bench.py
+# --copy-calib`: FETCH_SIZE 524301.7 KiB, WRITE_SIZE 1048576.0 KiB per copy).  The
+# figures hold for the kernel sources they were taken on only (SHA-256 over the files
+# below); for any other source the traffic is reported as unknown.
 DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "4268cd16915aa61e829dd975d27d51fa96da7cd3e03e560fdd0bf50495c19f0f",
-    "fetch_kib": 136031.2, "write_kib": 269312.0,
-    "fetch_scale": 1048576.0 / 524301.8, "write_scale": 1048576.0 / 1048576.0,
+    "sha256": "61b5c9a2fab42a5377e994e736cce08922c41a96c5546352cb5b57be758e3b3e",
+    "fetch_kib": 136084.5, "write_kib": 269312.0,
+    "fetch_scale": 1048576.0 / 524301.7, "write_scale": 1048576.0 / 1048576.0,
 }
 
 
