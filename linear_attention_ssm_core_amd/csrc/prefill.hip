@@ -124,20 +124,20 @@ __device__ __forceinline__ bf16x8 zero8() {
 // row into the chunk, and rows past the chunk end only ever meet exact zeros
 // (T has zero rows and columns for them), so no exec-masked load -- and no
 // waitcnt that would drain the next chunk's prefetch -- is needed.
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
+// Eight fp32 values -> bf16 hi and lo operands (packed conversions).
+__device__ __forceinline__ void split8f(const floatx4 &a, const floatx4 &b, bf16x8 &hi, bf16x8 &lo) {
+  const Split2 s0 = split_bf16_2(a[0], a[1]), s1 = split_bf16_2(a[2], a[3]);
+  const Split2 s2 = split_bf16_2(b[0], b[1]), s3 = split_bf16_2(b[2], b[3]);
+  hi = as_bf16x8(make_uint4(s0.hi, s1.hi, s2.hi, s3.hi));
+  lo = as_bf16x8(make_uint4(s0.lo, s1.lo, s2.lo, s3.lo));
+}
 __device__ __forceinline__ void frag8(const bf16 *p, bf16x8 &hi, bf16x8 &lo) {
   hi = *reinterpret_cast<const bf16x8 *>(p);
   lo = zero8();
 }
 __device__ __forceinline__ void frag8(const float *p, bf16x8 &hi, bf16x8 &lo) {
-  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16 h, l;
-    split_bf16(v[e], h, l);
-    hi[e] = h;
-    lo[e] = l;
-  }
+  split8f(reinterpret_cast<const floatx4 *>(p)[0], reinterpret_cast<const floatx4 *>(p)[1], hi, lo);
 }
 
 // acc += (ah + al)(bh + bl) without the al*bl term; *_SPLIT = false means the
@@ -152,14 +152,9 @@ __device__ __forceinline__ floatx4 mma(floatx4 acc, const bf16x8 &ah, const bf16
 
 // Four consecutive fp32 values -> bf16 hi/lo, stored as two 8-byte words.
 __device__ __forceinline__ void store_split4(bf16 *hi, bf16 *lo, const float v[4]) {
-  union {
-    bf16 b[4];
-    uint2 u;
-  } H, L;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) split_bf16(v[e], H.b[e], L.b[e]);
-  *reinterpret_cast<uint2 *>(hi) = H.u;
-  *reinterpret_cast<uint2 *>(lo) = L.u;
+  const Split2 a = split_bf16_2(v[0], v[1]), b = split_bf16_2(v[2], v[3]);
+  *reinterpret_cast<uint2 *>(hi) = make_uint2(a.hi, b.hi);
+  *reinterpret_cast<uint2 *>(lo) = make_uint2(a.lo, b.lo);
 }
 
 // ---- 1. chunk table ----------------------------------------------------------
@@ -315,8 +310,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     s_gam[lane] = la;
     s_bb[lane] = bb;
     const float glast = __shfl(la, kC - 1);
-    s_dec[lane] = expf(glast - la);
-    Gam[lane] = expf(la);
+    s_dec[lane] = __expf(glast - la);
+    Gam[lane] = __expf(la);
   }
   // K rows for the K^T staging of phase D: lane = token, 8 consecutive columns
   // per load (columns 8 (wave + 4 m) ..), written to LDS only once Abar is dead.
@@ -369,12 +364,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
         ak = mma<SP, SP>(ak, kih[ks], kil[ks], kh[slot][ks], kl[slot][ks]);
       }
     }
+    if (tj <= ti) {
+      const float gc = s_gam[16 * tj + lr];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = 16 * ti + 4 * lg + rr, c = 16 * tj + lr;
-      const float dec = expf(s_gam[r] - s_gam[c]);
-      s_A[r][c] = (c < r) ? s_bb[r] * dec * ak[rr] : 0.0f;
-      mv[tj][rr] = (c <= r) ? dec * aq[rr] : 0.0f;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = 16 * ti + 4 * lg + rr, c = 16 * tj + lr;
+        const float dec = __expf(s_gam[r] - gc);  // c <= r: the argument is <= 0
+        s_A[r][c] = (c < r) ? s_bb[r] * dec * ak[rr] : 0.0f;
+        mv[tj][rr] = (c <= r) ? dec * aq[rr] : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        s_A[16 * ti + 4 * lg + rr][16 * tj + lr] = 0.0f;
+        mv[tj][rr] = 0.0f;
+      }
     }
   }
   __syncthreads();
@@ -446,18 +450,21 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   bf16x8 th[2], tl[2], dh[2], dl[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
+    uint32_t wth[4], wtl[4], wdh[4], wdl[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 8; e += 2) {
       const int sr = 8 * lg + 32 * ks + e;
-      const float tv = s_L[sr][jrow] * bj;
-      bf16 hi, lo;
-      split_bf16(tv, hi, lo);
-      th[ks][e] = hi;
-      tl[ks][e] = lo;
-      split_bf16(s_dec[sr] * tv, hi, lo);
-      dh[ks][e] = hi;
-      dl[ks][e] = lo;
+      const float t0v = s_L[sr][jrow] * bj, t1v = s_L[sr + 1][jrow] * bj;
+      const Split2 ts = split_bf16_2(t0v, t1v), ds = split_bf16_2(s_dec[sr] * t0v, s_dec[sr + 1] * t1v);
+      wth[e / 2] = ts.hi;
+      wtl[e / 2] = ts.lo;
+      wdh[e / 2] = ds.hi;
+      wdl[e / 2] = ds.lo;
     }
+    th[ks] = as_bf16x8(make_uint4(wth[0], wth[1], wth[2], wth[3]));
+    tl[ks] = as_bf16x8(make_uint4(wtl[0], wtl[1], wtl[2], wtl[3]));
+    dh[ks] = as_bf16x8(make_uint4(wdh[0], wdh[1], wdh[2], wdh[3]));
+    dl[ks] = as_bf16x8(make_uint4(wdl[0], wdl[1], wdl[2], wdl[3]));
   }
   __syncthreads();
   // M (hi/lo) into R0, K^T (rows past the chunk end zero: E must see exact zeros) into R1
@@ -560,24 +567,13 @@ __device__ __forceinline__ void load8(Raw8<float> &r, const float *p) {
   r.w0 = reinterpret_cast<const uint4 *>(p)[0];
   r.w1 = reinterpret_cast<const uint4 *>(p)[1];
 }
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 // as an MFMA operand: bf16 is exact (lo unused), fp32 splits into hi + lo
 __device__ __forceinline__ void split8(const Raw8<bf16> &r, bf16x8 &hi, bf16x8 &lo) {
   hi = as_bf16x8(r.w);
   lo = hi;
 }
 __device__ __forceinline__ void split8(const Raw8<float> &r, bf16x8 &hi, bf16x8 &lo) {
-  const floatx4 a = __builtin_bit_cast(floatx4, r.w0), b = __builtin_bit_cast(floatx4, r.w1);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16 h0, l0, h1, l1;
-    split_bf16(a[e], h0, l0);
-    split_bf16(b[e], h1, l1);
-    hi[e] = h0;
-    lo[e] = l0;
-    hi[4 + e] = h1;
-    lo[4 + e] = l1;
-  }
+  split8f(__builtin_bit_cast(floatx4, r.w0), __builtin_bit_cast(floatx4, r.w1), hi, lo);
 }
 // One activation kept raw: bf16 as its 16 bits, fp32 as is.
 template <typename TY>
