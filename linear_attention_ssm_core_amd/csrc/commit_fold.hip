@@ -7,12 +7,14 @@
 namespace gdn {
 namespace {
 
-// The state copy of a sequence is split into tiles of 256 threads x 8 16-byte
-// vectors (32 KiB, 8 loads in flight per thread), one workgroup each: 64
-// workgroups per 2 MiB state, so the ~50 copies of a verify batch spread over the
-// whole chip.  blockIdx.y < the tile count copies a tile; the rest rebuild
-// conv-state channels.
-constexpr int kCommitTile = 256 * 8;  // 16-byte vectors per copy workgroup
+// The state copy of a sequence is split into tiles of 256 16-byte vectors (4 KiB),
+// one vector per thread: many short workgroups, dispatched in address order, keep
+// the copies that are in flight at any moment close together, an order the HBM
+// read and write streams serve faster than long workgroups each sweeping its own
+// region (a cache-cold 4 GiB copy: 6.2 TB/s with one vector per thread, 5.3 with
+// sixteen).  blockIdx.x < the tile count copies a tile; the rest rebuild
+// conv-state channels; blockIdx.y is the sequence.
+constexpr int kCommitTile = 256;  // 16-byte vectors per copy workgroup
 constexpr int kMaxFoldRows = 16;
 
 // The conv state of sequence i becomes the last K-1 rows of
@@ -40,27 +42,19 @@ __device__ __forceinline__ void advance_ring(const Geometry &geo, void *const *c
 // Commit: copy the state after the last accepted row into table 0.
 template <typename TE>
 __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4, int ntiles) {
-  const int i = blockIdx.x;
+  const int i = blockIdx.y;
   const int k = p.cu[i + 1] - p.cu[i];
   const int na = p.n_accepted[i];
   if (na < 1 || na > k) return;  // outside the caller's contract: sequence untouched
-  if ((int)blockIdx.y < ntiles) {
+  if ((int)blockIdx.x < ntiles) {
     if (na == k) return;  // table 0 already holds the last state
     // (native 4-float vectors: the struct-based float4 array ends up in scratch)
     const gptr<const floatx4> src = to_global(static_cast<const floatx4 *>(p.tables[na * kTableSeqs + i]));
     const gptr<floatx4> dst = to_global(static_cast<floatx4 *>(p.tables[i]));
-    const int64_t beg = (int64_t)blockIdx.y * kCommitTile;
-    if (beg + kCommitTile <= n4) {  // a whole tile, without conditions
-      floatx4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = src[beg + threadIdx.x + u * 256];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) dst[beg + threadIdx.x + u * 256] = v[u];
-    } else {
-      for (int64_t idx = beg + threadIdx.x; idx < n4; idx += 256) dst[idx] = src[idx];
-    }
+    const int64_t idx = (int64_t)blockIdx.x * kCommitTile + threadIdx.x;
+    if (idx < n4) dst[idx] = src[idx];
   } else {
-    advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.y - ntiles);
+    advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.x - ntiles);
   }
 }
 
@@ -68,11 +62,10 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4,
 // accepted rows from the stash in order (the verify's rank-1 update, in the same
 // operation order), and written once; the other blocks advance the conv state.
 // Thread t holds
-// column quad t % (D/4) of the D^2/1024 consecutive rows from (t / (D/4)) D^2/1024,
-// as in the verify.
+// column quad t % (D/4) of the rows state_row(t / (D/4), .), as in the verify.
 template <int D, typename TE, typename TS>
 __global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
-  constexpr int CQ = D / 4, RG = kSlot / CQ, RPT = D / RG;
+  constexpr int CQ = HeadLayout<D>::CQ, RPT = HeadLayout<D>::RPT;
   __shared__ float s_k[kMaxFoldRows][D], s_u[kMaxFoldRows][D], s_a[kMaxFoldRows];
   const int i = blockIdx.x;
   const int r0 = p.cu[i];
@@ -89,7 +82,7 @@ __global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
   const gptr<TS> S = to_global(static_cast<TS *>(p.states[i])) + (size_t)h * D * D;
   typename StateIO<TS>::raw st_raw[RPT];
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S + (size_t)(rg * RPT + rr) * D + 4 * cq);
+  for (int rr = 0; rr < RPT; ++rr) st_raw[rr] = StateIO<TS>::load(S + (size_t)state_row<D>(rg, rr) * D + 4 * cq);
   const gptr<const float> stash = to_global(p.stash) + (size_t)r0 * p.stash_row;
   for (int e = t; e < na * D; e += kSlot) {
     const int r = e / D, j = e - r * D;
@@ -106,10 +99,10 @@ __global__ __launch_bounds__(kSlot) void fold_kernel(FoldLaunch p) {
     const floatx4 u = *reinterpret_cast<const floatx4 *>(&s_u[r][4 * cq]);
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr)
-      st_reg[rr] = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, s_k[r][rg * RPT + rr], u));
+      st_reg[rr] = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, s_k[r][state_row<D>(rg, rr)], u));
   }
 #pragma unroll
-  for (int rr = 0; rr < RPT; ++rr) StateIO<TS>::store(S + (size_t)(rg * RPT + rr) * D + 4 * cq, st_reg[rr]);
+  for (int rr = 0; rr < RPT; ++rr) StateIO<TS>::store(S + (size_t)state_row<D>(rg, rr) * D + 4 * cq, st_reg[rr]);
 }
 
 template <int D, typename TE>
@@ -136,7 +129,7 @@ hipError_t launch_commit(const CommitLaunch &p, hipStream_t stream) {
   const int64_t n4 = (int64_t)p.geo.Hv * p.geo.D * p.geo.D / (p.state_f16 ? 8 : 4);
   const int ntiles = (int)((n4 + kCommitTile - 1) / kCommitTile);
   const int nblk_ring = (p.geo.conv_dim + 255) / 256;
-  const dim3 grid(p.n, ntiles + nblk_ring), block(256);
+  const dim3 grid(ntiles + nblk_ring, p.n), block(256);
   if (p.geo.act_bf16)
     hipLaunchKernelGGL((commit_kernel<uint16_t>), grid, block, 0, stream, p, n4, ntiles);
   else
