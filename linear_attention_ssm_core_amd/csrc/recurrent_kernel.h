@@ -83,6 +83,30 @@ __device__ __forceinline__ floatx4 rank1_update(floatx4 s, float a, float k, flo
   return r;
 }
 
+// The sequence that workgroup `rank` of a multi-row launch takes: sequences go
+// longest first (rank r is the sequence with r sequences ahead of it, a longer one
+// or an equally long one of lower index), so the long ones do not trail at the end
+// of the grid.  n <= 128: lane l holds the lengths of sequences l and l + 64; each
+// wave tests its share of the candidates, counting the sequences ahead of one with
+// two ballots.  (length, index) is a strict total order whatever the lengths, so
+// the ranks are a permutation of 0 .. n-1 and exactly one candidate matches.
+// Block-uniform result (read back through LDS after a barrier).
+__device__ __forceinline__ int seq_of_rank(const int32_t *cu, int n, int rank, int nthreads, int *s_seq) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const bool v0 = lane < n, v1 = lane + kWave < n;  // lanes past n are never ahead
+  const int l0 = v0 ? cu[lane + 1] - cu[lane] : 0;
+  const int l1 = v1 ? cu[lane + kWave + 1] - cu[lane + kWave] : 0;
+  for (int t = wave; t < n; t += nthreads / kWave) {
+    const int lt = t < kWave ? __shfl(l0, t) : __shfl(l1, t - kWave);
+    const bool a0 = v0 && (l0 > lt || (l0 == lt && lane < t));
+    const bool a1 = v1 && (l1 > lt || (l1 == lt && lane + kWave < t));
+    const int ahead = __popcll(__ballot(a0)) + __popcll(__ballot(a1));
+    if (ahead == rank && lane == 0) *s_seq = t;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*s_seq);
+}
+
 // Thread layout over a d x d head of the state: kSlot threads, each holding RPT
 // rows of one column quad (4 consecutive columns).  Row group rg's rows are
 // state_row(rg, 0 .. RPT-1).  The RGW row groups that share a wave (in the layout
@@ -204,28 +228,13 @@ void recurrent_kernel(RecurrentLaunch p) {
     r0 = i;
     nrows = 1;
   } else {
-    // several rows per sequence: workgroups take sequences longest first, so the
-    // long ones do not trail at the end of the grid (ranks of the <= 128 lengths,
-    // ties by index)
-    __shared__ int s_cu[kTableSeqs + 1];
+    // several rows per sequence: workgroups take sequences longest first
     __shared__ int s_seq;
-    for (int t = tid; t <= p.n; t += NT) s_cu[t] = p.cu[t];
-    __syncthreads();
-    for (int t = tid; t < p.n; t += NT) {
-      const int kt = s_cu[t + 1] - s_cu[t];
-      int rk = 0;
-      for (int s2 = 0; s2 < p.n; ++s2) {
-        const int k2 = s_cu[s2 + 1] - s_cu[s2];
-        rk += (k2 > kt) || (k2 == kt && s2 < t);
-      }
-      if (rk == rank) s_seq = t;
-    }
-    __syncthreads();
+    i = seq_of_rank(p.cu, p.n, rank, NT, &s_seq);
     // uniform over the block: read into scalar registers, so that every address
     // derived from them is scalar too
-    i = __builtin_amdgcn_readfirstlane(s_seq);
-    r0 = __builtin_amdgcn_readfirstlane(s_cu[i]);
-    nrows = __builtin_amdgcn_readfirstlane(s_cu[i + 1]) - r0;
+    r0 = __builtin_amdgcn_readfirstlane(p.cu[i]);
+    nrows = __builtin_amdgcn_readfirstlane(p.cu[i + 1]) - r0;
     nrows = nrows < 0 ? 0 : (nrows > MAXR ? MAXR : nrows);
   }
   if (nrows == 0) return;  // uniform over the block
