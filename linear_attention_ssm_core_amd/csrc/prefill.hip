@@ -32,14 +32,15 @@
 //      then E and MT on MFMA.  E and MT go to the workspace as bf16 hi/lo pairs in MFMA
 //      fragment order, so the next kernel loads each fragment as one contiguous 1 KiB
 //      block.
-//   3. spine_kernel, one workgroup per (sequence, value head, 16-column block of d_v):
-//      the serial pass over the chunks.  Two "chain" waves keep the state block in
-//      MFMA accumulators and carry h -> K h -> X -> E X -> h entirely in registers
-//      (the only exchange per chunk is the sum of their two halves of K h, through
-//      LDS); two "output" waves compute O one chunk behind.  See the comment at the
-//      kernel.  Columns of h evolve independently, so a 128-wide state splits into 8
-//      workgroups; those of the value heads of one key head are mapped onto one XCD
-//      so they share its operands through one L2.
+//   3. spine_kernel, one workgroup per (sequence, value head, 16- or 32-column block
+//      of d_v): the serial pass over the chunks.  d_k / 32 "chain" waves keep the
+//      state block in MFMA accumulators (one d_k k-step each) and carry
+//      h -> K h -> X -> E X -> h in registers; the exchanges per chunk are the sum of
+//      their partial K h and the X each of them forms for one token tile, through
+//      LDS.  Four "output" waves compute O one chunk behind.  See the comment at
+//      the kernel.  Columns of h evolve independently, so a 128-wide state splits
+//      into 8 (or 4) workgroups; those of the value heads of one key head are
+//      mapped onto one XCD so they share its operands through one L2.
 // Precision: fp32-derived operands (h, X, T, E, MT, and fp32 activations) enter
 // MFMA as bf16 hi + lo; a product takes hi*hi + hi*lo + lo*hi, about 2^-16
 // relative, which keeps states within 1e-4 of the fp64 recurrence.
