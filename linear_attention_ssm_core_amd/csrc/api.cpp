@@ -104,7 +104,9 @@ gdn_status plan_prefill(const gdn_prefill_args *a, PrefillPlan *plan) {
   const Geometry &g = plan->geo;
   plan->y_bytes = plan->fused_front ? align256((size_t)T * g.conv_dim * 4) : 0;
   plan->o_bytes = plan->epilogue ? align256((size_t)T * g.Hv * g.D * 4) : 0;
-  plan->core_bytes = a->num_seqs > 0 ? align256(gdn::prefill_core_workspace(g, a->num_seqs, T)) : 0;
+  // y: fp32 from the fused front, else the caller's rows in the activation dtype
+  const bool y_bf16 = !plan->fused_front && g.act_bf16;
+  plan->core_bytes = a->num_seqs > 0 ? align256(gdn::prefill_core_workspace(g, a->num_seqs, T, y_bf16)) : 0;
   plan->total = plan->y_bytes + plan->o_bytes + plan->core_bytes;
   return GDN_OK;
 }

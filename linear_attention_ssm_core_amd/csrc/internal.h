@@ -110,7 +110,7 @@ struct PrefillLaunch {
   void *workspace;              // prefill workspace (chunk tables and per-chunk operands)
 };
 // Bytes of workspace the chunk kernels need for n sequences and T tokens.
-size_t prefill_core_workspace(const Geometry &geo, int n, int64_t T);
+size_t prefill_core_workspace(const Geometry &geo, int n, int64_t T, bool y_bf16);
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream);
 
 // Scratch of the allocation-free prefill: a device array of this many bytes per

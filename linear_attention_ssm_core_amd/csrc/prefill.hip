@@ -65,6 +65,13 @@ int64_t max_chunks(int n, int64_t T) { return T / kC + n; }
 __host__ __device__ constexpr size_t unit_bytes(int D) { return a256((size_t)4 * D * kC + (size_t)4 * kC * kC + 256); }
 // Element offset of lane `lane`'s 8 values of fragment (tile, ks) with nks k-steps.
 __host__ __device__ constexpr int frag_off(int tile, int ks, int nks, int lane) { return ((tile * nks + ks) * 64 + lane) * 8; }
+// Per (chunk, key head): the chunk's K and Q rows as the spine's MFMA A operands,
+// bf16 in fragment order [tile][k-step][lane][8] with the tiles' rows in the order
+// row_of (below), rows past the chunk's end zero: K then Q, each one plane (bf16
+// activations, exact) or a hi and a lo plane (fp32 activations).  The prep writes
+// them; the spine then loads every operand fragment as one contiguous 1 KiB block
+// instead of 16-byte pieces of 16 rows a row stride apart.
+__host__ __device__ constexpr size_t kq_bytes(int D, int planes) { return a256((size_t)planes * 2 * kC * D * 2); }
 
 // Row order of the spine's operands.  A 16x16 MFMA result leaves lane (n, g)
 // holding rows 4g .. 4g + 3 of column n; the B operand of a 16x16x32 product wants
@@ -248,7 +255,7 @@ struct PrepLds {
 };
 
 template <int D, typename TY>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, char *units) {
+__global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, char *units, char *kq) {
   constexpr bool SP = std::is_same<TY, float>::value;
   constexpr int NP = SP ? 2 : 1;
   constexpr int KS = D / 32;
@@ -350,6 +357,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     }
   }
   __syncthreads();
+  // The chunk's K and Q rows of tile ti for the spine (one value head per key head
+  // writes them): natural row r = 16 ti + lr is operand row m of spine tile tt, with
+  // row_of(tt, m) = r; rows past the chunk's end are written as zeros.
+  if (h % G == 0) {
+    bf16 *dst = reinterpret_cast<bf16 *>(kq + ((size_t)cidx * Hk + g) * kq_bytes(D, NP));
+    const int r = 16 * ti + lr;
+    const bool live = r < L;
+    const int tt = 2 * (r >> 5) + ((r >> 2) & 1), m = 4 * ((r & 31) >> 3) + (r & 3);
+    const bf16x8 z8 = zero8();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int fo = frag_off(tt, ks, KS, m + 16 * lg);
+      *reinterpret_cast<bf16x8 *>(dst + fo) = live ? kih[ks] : z8;
+      *reinterpret_cast<bf16x8 *>(dst + NP * kC * D + fo) = live ? qh[ks] : z8;
+      if constexpr (SP) {
+        *reinterpret_cast<bf16x8 *>(dst + kC * D + fo) = live ? kil[ks] : z8;
+        *reinterpret_cast<bf16x8 *>(dst + 3 * kC * D + fo) = live ? ql[ks] : z8;
+      }
+    }
+  }
 
   // ---- B: Q K^T and K K^T for row block ti; M stays in registers until phase D ----
   float mv[4][4];  // M[16 ti + 4 lg + rr][16 tj + lr]
@@ -631,13 +658,14 @@ __device__ __forceinline__ void bstore(Rsrc r, uint32_t off, bf16 v) {
 }
 
 template <int D, int NC, typename TY, typename TO>
-__global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, const char *units) {
+__global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, const char *units, const char *kq) {
   constexpr bool SP = std::is_same<TY, float>::value;
   constexpr int KS = D / 32;        // k-steps over d_k = chain waves
   constexpr int CB = kCB * NC;      // state columns per workgroup (NC tiles of 16)
   constexpr int NCB = D / CB;       // column blocks per head
   constexpr int TPW = 4 / KS;       // token tiles whose X a chain wave forms
   constexpr int NT = SP ? 3 : 2;    // terms of a product with h: hi hi, hi lo (, lo hi)
+  constexpr int NP = SP ? 2 : 1;    // planes of the K and Q fragments: hi (, lo)
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   // Consecutive workgroups are dispatched round-robin over the 8 XCDs; within
   // each group of 8 * G * NCB, remap so that one XCD receives the NCB column blocks
@@ -675,6 +703,8 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 
   const TY *y = static_cast<const TY *>(p.y);
   auto unit_of = [&](int c) { return units + ((size_t)(c_first + c) * Hv + h) * unit_bytes(D); };
+  // K and Q fragments of chunk c (key head g)
+  auto kq_of = [&](int c) { return make_rsrc(kq + ((size_t)(c_first + c) * Hk + g) * kq_bytes(D, NP), kq_bytes(D, NP)); };
   auto gam_of = [&](int c) {
     return reinterpret_cast<const float *>(reinterpret_cast<const bf16 *>(unit_of(c)) + 2 * D * kC + 2 * kC * kC);
   };
@@ -702,7 +732,6 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     }
     // ---------------- chain waves ----------------
     const int cw = wave;
-    const int kcol = (Hk + g) * D + 32 * cw;  // this wave's d_k columns of K
     // the sequence's state: fp32, or binary16 widened here and narrowed at the end;
     // result tile (i, ct) of this wave holds d_k rows row_of(2 cw + i, 4 lg + r) of
     // column 16 ct + lr of the block
@@ -733,15 +762,15 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
           for (int r = 0; r < 4; ++r) hacc[i][ct][r] = hs[(size_t)row_of(2 * cw + i, 4 * lg + r) * D + 16 * ct];
     }
-    Raw8<TY> kf[4];               // K rows of token tile tt (row order row_of), this wave's k-step
+    uint4 kf[4][NP];              // K fragments of token tile tt, this wave's k-step: hi (, lo)
     uint4 ef[2][2][2];            // E fragments: result tile, token k-step, hi / lo
     float gC = 0.0f;              // Gam_63
-    // per-lane byte offsets, the same for every chunk, within a token tile's rows
-    // (row_of(tt, m) = first row of tt + 8 (m / 4) + m % 4)
-    const uint32_t koff = ((8 * (lr >> 2) + (lr & 3)) * CD + kcol + 8 * lg) * (uint32_t)sizeof(TY);
     auto fetch_k = [&](int c) {
+      const Rsrc rk = kq_of(c);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) bload(kf[tt], tile_rows(c, tt), koff);
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) kf[tt][pl] = bload16(rk, 2 * (uint32_t)(pl * kC * D + frag_off(tt, cw, KS, lane)));
     };
     auto fetch_e = [&](int c) {
       const Rsrc ru = make_rsrc(unit_of(c), unit_bytes(D));
@@ -780,7 +809,10 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       {
         bf16x8 kh[4], kl[4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) split8(kf[tt], kh[tt], kl[tt]);
+        for (int tt = 0; tt < 4; ++tt) {
+          kh[tt] = as_bf16x8(kf[tt][0]);
+          kl[tt] = as_bf16x8(kf[tt][NP - 1]);  // (bf16: unused)
+        }
 #pragma unroll
         for (int term = 0; term < NT; ++term)
 #pragma unroll
@@ -873,13 +905,11 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   } else {
     // ---------------- output waves ----------------
     const int tt = wave - 4;  // token tile
-    const int qcol = g * D;
     TO *o = static_cast<TO *>(p.o);
     const size_t ostride = (size_t)Hv * D;
     const int ocol = h * D + CB * cb + lr;
     const uint32_t ooff = (uint32_t)((8 * lg * ostride + ocol) * sizeof(TO));
-    const uint32_t qoff = ((8 * (lr >> 2) + (lr & 3)) * CD + qcol + 8 * lg) * (uint32_t)sizeof(TY);
-    Raw8<TY> qf[2][KS];   // Q rows of the tile (row order row_of), all k-steps; chunk parity
+    uint4 qf[2][KS][NP];  // Q fragments of the tile, all k-steps, hi (, lo); chunk parity
     uint4 mf[2][2][2];    // MT fragments: chunk parity, token k-step, hi / lo
     floatx4 go[2];        // Gam of the tile's tokens; chunk parity
     Raw8<TY> vr[2];       // V of the tile for the chain waves: operand row vm, 8 columns from vc
@@ -890,10 +920,13 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     const uint32_t vof = ((8 * (vm >> 2) + (vm & 3)) * CD + 2 * Hk * D + h * D + CB * cb + vc) * (uint32_t)sizeof(TY);
     auto fetch_q = [&](auto par, int c) {
       constexpr int PAR = decltype(par)::value;
-      const Rsrc rt = tile_rows(c, tt);
+      const Rsrc rq = kq_of(c);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) bload(qf[PAR][s], rt, qoff + 32 * s * (uint32_t)sizeof(TY));
-      bload(vr[PAR], rt, vof);
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+          qf[PAR][s][pl] = bload16(rq, 2 * (uint32_t)((NP + pl) * kC * D + frag_off(tt, s, KS, lane)));
+      bload(vr[PAR], tile_rows(c, tt), vof);
       go[PAR] = bloadf4(make_rsrc(unit_of(c), unit_bytes(D)), kGamOff + 4 * (uint32_t)row_of(tt, 4 * lg));
     };
     // the chunk's V (in the activation dtype) and Gam to LDS for the chain waves
@@ -919,8 +952,7 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       for (int ct = 0; ct < NC; ++ct) O[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        bf16x8 qh, ql;
-        split8(qf[PAR][s], qh, ql);
+        const bf16x8 qh = as_bf16x8(qf[PAR][s][0]), ql = as_bf16x8(qf[PAR][s][NP - 1]);
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
           const bf16x8 hh = s_H[s][0][ct][lane], hl = s_H[s][1][ct][lane];
@@ -979,13 +1011,14 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
   tb.implicit = p.n == 1;
   tb.T = (int)p.T;
   char *units = ws + a256(tables_bytes(p.n, NC));
+  char *kq = units + (size_t)NC * p.geo.Hv * unit_bytes(D);
   hipError_t e = hipSuccess;
   if (!tb.implicit) {
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(256), 0, stream, p.cu, p.n, NC, tb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hv)), dim3(256), 0, stream, p, tb, units);
+  hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hv)), dim3(256), 0, stream, p, tb, units, kq);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 16-column blocks while that is what it takes to give every CU a workgroup
@@ -994,10 +1027,10 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
   const int64_t wg16 = (int64_t)p.n * p.geo.Hv * (D / kCB);
   if (D >= 32 && wg16 > 2 * kSpineWideMinBlocks)
     hipLaunchKernelGGL((spine_kernel<D, 2, TY, TO>), dim3((unsigned)(wg16 / 2)), dim3(512), 0, stream, p, tb,
-                       static_cast<const char *>(units));
+                       static_cast<const char *>(units), static_cast<const char *>(kq));
   else
     hipLaunchKernelGGL((spine_kernel<D, 1, TY, TO>), dim3((unsigned)wg16), dim3(512), 0, stream, p, tb,
-                       static_cast<const char *>(units));
+                       static_cast<const char *>(units), static_cast<const char *>(kq));
   return hipGetLastError();
 }
 
@@ -1050,9 +1083,10 @@ hipError_t prefill_scratch(void **ptr) {
   return hipSuccess;
 }
 
-size_t prefill_core_workspace(const Geometry &geo, int n, int64_t T) {
+size_t prefill_core_workspace(const Geometry &geo, int n, int64_t T, bool y_bf16) {
   const int64_t NC = max_chunks(n, T);
-  return a256(tables_bytes(n, NC)) + (size_t)NC * geo.Hv * unit_bytes(geo.D);
+  return a256(tables_bytes(n, NC)) + (size_t)NC * geo.Hv * unit_bytes(geo.D) +
+         (size_t)NC * geo.Hk * kq_bytes(geo.D, y_bf16 ? 1 : 2);
 }
 
 hipError_t launch_prefill(const PrefillLaunch &p, hipStream_t stream) {
