@@ -401,12 +401,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
         s_A[r][c] = (c < r) ? s_bb[r] * dec * ak[rr] : 0.0f;
         mv[tj][rr] = (c <= r) ? dec * aq[rr] : 0.0f;
       }
-    } else {
+    } else {  // above the diagonal: M is zero, Abar's tile is never read
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        s_A[16 * ti + 4 * lg + rr][16 * tj + lr] = 0.0f;
-        mv[tj][rr] = 0.0f;
-      }
+      for (int rr = 0; rr < 4; ++rr) mv[tj][rr] = 0.0f;
     }
   }
   __syncthreads();
@@ -414,7 +411,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   // ---- C: L^-1 for L = I + Abar (unit lower triangular), fp32 ----
   // Level 1: the four 16x16 diagonal blocks, right-looking substitution (wave 0:
   // lane = block * 16 + column; after step m, x[m] is final and the updates of
-  // the rows below it are independent); the other waves clear the upper blocks.
+  // the rows below it are independent).  The blocks above the diagonal are never
+  // written: phase D, the only reader of those entries, masks them.
   if (wave == 0) {
     const int bk = lane / 16, c = lane % 16;
     float x[16];
@@ -426,11 +424,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       for (int r = m + 1; r < 16; ++r) x[r] -= s_A[16 * bk + r][16 * bk + m] * x[m];
 #pragma unroll
     for (int r = 0; r < 16; ++r) s_L[16 * bk + r][16 * bk + c] = x[r];
-  } else {
-    for (int e = tid - kWave; e < kC * kC; e += 256 - kWave) {
-      const int r = e / kC, c = e % kC;
-      if ((c >> 4) > (r >> 4)) s_L[r][c] = 0.0f;
-    }
   }
   __syncthreads();
   // Level 2: [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1] on the two 32x32 diagonal
@@ -482,7 +475,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const int sr = 8 * lg + 32 * ks + e;
-      const float t0v = s_L[sr][jrow] * bj, t1v = s_L[sr + 1][jrow] * bj;
+      // L^-1 is zero above its diagonal blocks (block row 2 ks + lg / 2 < block column wave)
+      const bool upper = wave > 2 * ks + (lg >> 1);
+      const float t0v = upper ? 0.0f : s_L[sr][jrow] * bj, t1v = upper ? 0.0f : s_L[sr + 1][jrow] * bj;
       const Split2 ts = split_bf16_2(t0v, t1v), ds = split_bf16_2(s_dec[sr] * t0v, s_dec[sr + 1] * t1v);
       wth[e / 2] = ts.hi;
       wtl[e / 2] = ts.lo;
