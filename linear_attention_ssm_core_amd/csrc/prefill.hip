@@ -759,7 +759,6 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     }
     uint4 kf[4][NP];              // K fragments of token tile tt, this wave's k-step: hi (, lo)
     uint4 ef[2][2][2];            // E fragments: result tile, token k-step, hi / lo
-    float gC = 0.0f;              // Gam_63
     auto fetch_k = [&](int c) {
       const Rsrc rk = kq_of(c);
 #pragma unroll
@@ -776,12 +775,18 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
           for (int hl = 0; hl < 2; ++hl)
             ef[i][s][hl] = bload16(ru, 2 * (uint32_t)(hl * D * kC + frag_off(2 * cw + i, s, 2, lane)));
-      gC = gam_of(c)[kC - 1];
     };
+    // The state first, then the operand loads in the order the loop body issues them
+    // (K, then E; kept so by scheduling barriers): both paths into the loop then reach
+    // its header with the same loads pending, so the compiler's waits there stay
+    // partial instead of a full vmcnt(0) that would stall on the operands just issued.
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the state has arrived
+    __builtin_amdgcn_sched_barrier(0);
     fetch_k(0);
+    __builtin_amdgcn_sched_barrier(0);
     fetch_e(0);
-    auto chain_chunk = [&](int c, auto par) {
-      constexpr int PAR = decltype(par)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    auto chain_chunk = [&](int c) {
       const int cn = min(c + 1, nch - 1);  // past the end: the last chunk again, unused
       // h as the B operand (hi, lo) of this wave's k-step; to LDS for the output waves
       bf16x8 hb[NC][2];
@@ -824,6 +829,9 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       }
       fetch_k(cn);
       __syncthreads();  // barrier 1
+      // Gam_63 of this chunk: row 63 = row_of(3, 15), held by lanes 48.. of tile 3 in
+      // component 3 (read before barrier 2: the output waves overwrite s_G after it)
+      const float gC = s_G[3][48][3];
       // X of the own token tiles: partials summed in wave order (the own one read
       // back too: picking it out of pp by the wave-dependent tile index would put pp
       // in scratch memory), then V - Gam P, split into this wave's half of the token
@@ -875,12 +883,10 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
                                    hacc[i][ct]);
       fetch_e(cn);
     };
+    // one chunk per iteration (no double buffer here): a single loop body keeps the
+    // compiler's waits at the loop header partial
 #pragma unroll 1
-    for (int c = 0; c < nch; c += 2) {
-      chain_chunk(c, P0());
-      if (c + 1 >= nch) break;
-      chain_chunk(c + 1, P1());
-    }
+    for (int c = 0; c < nch; ++c) chain_chunk(c);
     if (p.state_f16) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
