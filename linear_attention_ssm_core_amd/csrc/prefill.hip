@@ -242,16 +242,20 @@ __device__ __forceinline__ void store_tile(float *dst, int ld, const floatx4 &v,
   for (int rr = 0; rr < 4; ++rr) dst[(4 * lg + rr) * ld + lr] = sgn * v[rr];
 }
 
-// LDS of prep_kernel, three regions reused across its phases (41 KiB for bf16
-// activations, so three workgroups share a CU):
+// LDS of prep_kernel, three regions reused across its phases (41 KiB, so three
+// workgroups share a CU):
 //   R0  L^-1 (fp32, solve and the reads of T)       -> M hi/lo (bf16, MT products)
 //   R1  Abar (fp32, solve)                          -> K^T hi(/lo) (bf16, E products)
 //   R2  block-product scratch (solve), gates
+// With fp32 activations K^T is a hi/lo pair: it is staged half of d_k at a time
+// (NPASS = 2), which keeps R1 at Abar's size and the workgroup at three per CU
+// instead of two.
 constexpr int kLF = 72;  // fp32 row stride of L^-1 and Abar
-template <int D, int NP>
+template <int D, int NP, int NPASS>
 struct PrepLds {
+  static constexpr size_t kt = (size_t)NP * (D / NPASS) * kLP * 2;
   static constexpr size_t r0 = (size_t)kC * kLF * 4 > (size_t)2 * kC * kLP * 2 ? (size_t)kC * kLF * 4 : (size_t)2 * kC * kLP * 2;
-  static constexpr size_t r1 = (size_t)kC * kLF * 4 > (size_t)NP * D * kLP * 2 ? (size_t)kC * kLF * 4 : (size_t)NP * D * kLP * 2;
+  static constexpr size_t r1 = (size_t)kC * kLF * 4 > kt ? (size_t)kC * kLF * 4 : kt;
 };
 
 template <int D, typename TY>
@@ -261,6 +265,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   constexpr int KS = D / 32;
   constexpr int NTI = D / 16;
   constexpr int NIG = D / 8 / 4;  // groups of 8 K columns staged per wave
+  constexpr int NPASS = (SP && NIG % 2 == 0) ? 2 : 1;  // K^T staged in NPASS parts of d_k
+  constexpr int NTP = NTI / NPASS;                      // E tiles per part
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
   // Workgroups go round-robin over the 8 XCDs; within each group of 8 * G, remap so
   // that the G value heads of a key head (which read the same K and Q rows) run on
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   bf16 *MT_lo = MT_hi + kC * kC;
   float *Gam = reinterpret_cast<float *>(MT_lo + kC * kC);
 
-  using LDS = PrepLds<D, NP>;
+  using LDS = PrepLds<D, NP, NPASS>;
   __shared__ __align__(16) char s_r0[LDS::r0];
   __shared__ __align__(16) char s_r1[LDS::r1];
   __shared__ __align__(16) float s_Y[4][16][17];  // block-product scratch
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   float (*s_L)[kLF] = reinterpret_cast<float (*)[kLF]>(s_r0);
   bf16 (*s_M)[kC][kLP] = reinterpret_cast<bf16 (*)[kC][kLP]>(s_r0);  // [2][kC][kLP]
   float (*s_A)[kLF] = reinterpret_cast<float (*)[kLF]>(s_r1);
-  bf16 (*s_Kt)[D][kLP] = reinterpret_cast<bf16 (*)[D][kLP]>(s_r1);   // [NP][D][kLP]
+  bf16 (*s_Kt)[D / NPASS][kLP] = reinterpret_cast<bf16 (*)[D / NPASS][kLP]>(s_r1);  // [NP][D / NPASS][kLP]
 
   // ---- A: gates; every load of the kernel up front ----
   if (wave == 0) {
@@ -490,7 +496,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     dl[ks] = as_bf16x8(make_uint4(wdl[0], wdl[1], wdl[2], wdl[3]));
   }
   __syncthreads();
-  // M (hi/lo) into R0, K^T (rows past the chunk end zero: E must see exact zeros) into R1
+  // M (hi/lo) into R0, the first part of K^T (rows past the chunk end zero: E must see
+  // exact zeros) into R1
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   {
     const bool live = lane < L;
 #pragma unroll
-    for (int m = 0; m < NIG; ++m)
+    for (int m = 0; m < NIG / NPASS; ++m)
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         s_Kt[0][8 * (wave + 4 * m) + u][lane] = live ? kth[m][u] : (bf16)0.0f;
@@ -530,18 +537,35 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   }
   // E^T[j][i] = sum_s D_s T[s][j] K[s][i]; lane holds column i, rows j..j+3 -> E[i][j..j+3]
 #pragma unroll
-  for (int tix = 0; tix < NTI; ++tix) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int part = 0; part < NPASS; ++part) {
+    if (part > 0) {  // K^T rows [D/NPASS part, D/NPASS (part + 1)), once every wave is done with the last part
+      __syncthreads();
+      const bool live = lane < L;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 khh = *reinterpret_cast<const bf16x8 *>(&s_Kt[0][16 * tix + lr][8 * lg + 32 * ks]);
-      const bf16x8 kll = SP ? *reinterpret_cast<const bf16x8 *>(&s_Kt[NP - 1][16 * tix + lr][8 * lg + 32 * ks])
-                            : zero8();
-      acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
+      for (int m = part * (NIG / NPASS); m < (part + 1) * (NIG / NPASS); ++m)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = 8 * (wave + 4 * m) + u - part * (D / NPASS);
+          s_Kt[0][row][lane] = live ? kth[m][u] : (bf16)0.0f;
+          if (SP) s_Kt[NP - 1][row][lane] = live ? ktl[m][u] : (bf16)0.0f;
+        }
+      __syncthreads();
     }
-    const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    const int fo = pfrag_off(16 * tix + lr, 16 * wave + 4 * lg);
-    store_split4(E_hi + fo, E_lo + fo, v);
+#pragma unroll
+    for (int tp = 0; tp < NTP; ++tp) {
+      const int tix = part * NTP + tp;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 khh = *reinterpret_cast<const bf16x8 *>(&s_Kt[0][16 * tp + lr][8 * lg + 32 * ks]);
+        const bf16x8 kll = SP ? *reinterpret_cast<const bf16x8 *>(&s_Kt[NP - 1][16 * tp + lr][8 * lg + 32 * ks])
+                              : zero8();
+        acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
+      }
+      const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+      const int fo = pfrag_off(16 * tix + lr, 16 * wave + 4 * lg);
+      store_split4(E_hi + fo, E_lo + fo, v);
+    }
   }
 }
 
