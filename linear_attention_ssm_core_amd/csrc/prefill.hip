@@ -259,7 +259,7 @@ struct PrepLds {
 };
 
 template <int D, typename TY>
-__global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, char *units, char *kq) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prep_kernel(PrefillLaunch p, Tables tb, char *units, char *kq) {
   constexpr bool SP = std::is_same<TY, float>::value;
   constexpr int NP = SP ? 2 : 1;
   constexpr int KS = D / 32;
@@ -267,50 +267,39 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
   constexpr int NIG = D / 8 / 4;  // groups of 8 K columns staged per wave
   constexpr int NPASS = (SP && NIG % 2 == 0) ? 2 : 1;  // K^T staged in NPASS parts of d_k
   constexpr int NTP = NTI / NPASS;                      // E tiles per part
+  constexpr int kMaxG = 4;                              // value heads per key head
   const int Hv = p.geo.Hv, Hk = p.geo.Hk, G = Hv / Hk, CD = p.geo.conv_dim;
-  // Workgroups go round-robin over the 8 XCDs; within each group of 8 * G, remap so
-  // that the G value heads of a key head (which read the same K and Q rows) run on
-  // one XCD and share them through its L2.
-  int b = blockIdx.x;
-  {
-    const int nb = gridDim.x, grp = 8 * G;
-    if (b < nb - nb % grp) {
-      const int r = b % grp;
-      b = (b - r) + (r % 8) * G + r / 8;
-    }
-  }
-  const int cidx = b / Hv, h = b - cidx * Hv;
+  // One workgroup per (chunk, key head): the G value heads of a key head share the
+  // chunk's K and Q rows and their Gram matrices Q K^T and K K^T (only the gates
+  // differ), so those are loaded and formed once; the solve and the E and MT
+  // products then run once per value head.
+  const int cidx = blockIdx.x / Hk, g = blockIdx.x - cidx * Hk;
   const int seq = tb.implicit ? (cidx * kC < tb.T ? 0 : -1) : tb.chunk_seq[cidx];
   if (seq < 0) return;
   const int t0 = tb.implicit ? cidx * kC : tb.chunk_start[cidx];
   const int L = tb.implicit ? min(kC, tb.T - t0) : tb.chunk_len[cidx];
-  const int g = h / G;
   const int tid = threadIdx.x, lane = tid % kWave, lr = lane % 16, lg = lane / 16;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const TY *y = static_cast<const TY *>(p.y);
   const TY *Qb = y + (size_t)t0 * CD + (size_t)g * D;
   const TY *Kb = y + (size_t)t0 * CD + (size_t)(Hk + g) * D;
-
-  char *unit = units + ((size_t)cidx * Hv + h) * unit_bytes(D);
-  bf16 *E_hi = reinterpret_cast<bf16 *>(unit);
-  bf16 *E_lo = E_hi + D * kC;
-  bf16 *MT_hi = E_lo + D * kC;
-  bf16 *MT_lo = MT_hi + kC * kC;
-  float *Gam = reinterpret_cast<float *>(MT_lo + kC * kC);
+  auto unit_of = [&](int hv) { return units + ((size_t)cidx * Hv + hv) * unit_bytes(D); };
 
   using LDS = PrepLds<D, NP, NPASS>;
   __shared__ __align__(16) char s_r0[LDS::r0];
   __shared__ __align__(16) char s_r1[LDS::r1];
   __shared__ __align__(16) float s_Y[4][16][17];  // block-product scratch
-  __shared__ float s_gam[kC], s_bb[kC], s_dec[kC];
+  __shared__ float s_gam[kMaxG][kC], s_bb[kMaxG][kC], s_dec[kMaxG][kC];
   float (*s_L)[kLF] = reinterpret_cast<float (*)[kLF]>(s_r0);
   bf16 (*s_M)[kC][kLP] = reinterpret_cast<bf16 (*)[kC][kLP]>(s_r0);  // [2][kC][kLP]
   float (*s_A)[kLF] = reinterpret_cast<float (*)[kLF]>(s_r1);
   bf16 (*s_Kt)[D / NPASS][kLP] = reinterpret_cast<bf16 (*)[D / NPASS][kLP]>(s_r1);  // [NP][D / NPASS][kLP]
 
-  // ---- A: gates; every load of the kernel up front ----
-  if (wave == 0) {
-    const size_t gi = (size_t)(t0 + min(lane, L - 1)) * Hv + h;
+  // ---- A: gates of the G value heads (wave s: value head G g + s); every load of
+  // the shared part up front ----
+  if (wave < G) {
+    const int hv = g * G + wave;
+    const size_t gi = (size_t)(t0 + min(lane, L - 1)) * Hv + hv;
     const float a_raw = p.a[gi], b_raw = p.b[gi];
     // ln a, clamped at -30; from raw gate inputs ln a = -softplus(g) and b = sigmoid(beta)
     const float ln_a = p.gates_raw ? -(fmaxf(a_raw, 0.0f) + log1pf(expf(-fabsf(a_raw)))) : logf(a_raw);
@@ -321,23 +310,23 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       const float v = __shfl_up(la, off);
       if (lane >= off) la += v;
     }
-    s_gam[lane] = la;
-    s_bb[lane] = bb;
+    s_gam[wave][lane] = la;
+    s_bb[wave][lane] = bb;
     const float glast = __shfl(la, kC - 1);
-    s_dec[lane] = __expf(glast - la);
+    s_dec[wave][lane] = __expf(glast - la);
+    float *Gam = reinterpret_cast<float *>(unit_of(hv) + (size_t)2 * (2 * D * kC + 2 * kC * kC));
     Gam[lane] = __expf(la);
   }
   // K rows for the K^T staging of phase D: lane = token, 8 consecutive columns
-  // per load (columns 8 (wave + 4 m) ..), written to LDS only once Abar is dead.
-  // With fp32 activations every operand is a hi/lo pair: holding all of them from
-  // here on would take the whole register file (one workgroup per CU), so those
-  // staging rows are loaded in phase D and the K tiles of phase B one at a time.
+  // per load (columns 8 (wave + 4 m) ..), loaded again for each value head in its
+  // phase D (cache hits) rather than held through the solves.  With fp32
+  // activations every operand is a hi/lo pair: the K tiles of phase B are then
+  // loaded one at a time.
   bf16x8 kth[NIG], ktl[NIG];
   auto load_kt = [&]() {
 #pragma unroll
     for (int m = 0; m < NIG; ++m) frag8(Kb + (size_t)min(lane, L - 1) * CD + 8 * (wave + 4 * m), kth[m], ktl[m]);
   };
-  if constexpr (!SP) load_kt();
   // wave w owns row block w of Q K^T -> M and of K K^T -> Abar.  (Its own K rows
   // are loaded on their own: picking them out of kh by the wave index would be a
   // run-time index into a register array, i.e. scratch memory.)
@@ -362,11 +351,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
       for (int tj = 0; tj < 4; ++tj) load_ktile(tj, tj);
     }
   }
-  __syncthreads();
-  // The chunk's K and Q rows of tile ti for the spine (one value head per key head
-  // writes them): natural row r = 16 ti + lr is operand row m of spine tile tt, with
-  // row_of(tt, m) = r; rows past the chunk's end are written as zeros.
-  if (h % G == 0) {
+  // The chunk's K and Q rows of tile ti for the spine: natural row r = 16 ti + lr is
+  // operand row m of spine tile tt, with row_of(tt, m) = r; rows past the chunk's end
+  // are written as zeros.
+  {
     bf16 *dst = reinterpret_cast<bf16 *>(kq + ((size_t)cidx * Hk + g) * kq_bytes(D, NP));
     const int r = 16 * ti + lr;
     const bool live = r < L;
@@ -384,187 +372,204 @@ __global__ __launch_bounds__(256) void prep_kernel(PrefillLaunch p, Tables tb, c
     }
   }
 
-  // ---- B: Q K^T and K K^T for row block ti; M stays in registers until phase D ----
-  float mv[4][4];  // M[16 ti + 4 lg + rr][16 tj + lr]
+  // ---- B: the Gram tiles (ti, tj <= ti) of Q K^T and K K^T, shared by the value heads ----
+  floatx4 gq[4], gk[4];
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
-    floatx4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+    gq[tj] = floatx4{0.f, 0.f, 0.f, 0.f};
+    gk[tj] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (tj <= ti) {
       const int slot = SP ? 0 : tj;
       if constexpr (SP) load_ktile(tj, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        aq = mma<SP, SP>(aq, qh[ks], ql[ks], kh[slot][ks], kl[slot][ks]);
-        ak = mma<SP, SP>(ak, kih[ks], kil[ks], kh[slot][ks], kl[slot][ks]);
+        gq[tj] = mma<SP, SP>(gq[tj], qh[ks], ql[ks], kh[slot][ks], kl[slot][ks]);
+        gk[tj] = mma<SP, SP>(gk[tj], kih[ks], kil[ks], kh[slot][ks], kl[slot][ks]);
       }
     }
-    if (tj <= ti) {
-      const float gc = s_gam[16 * tj + lr];
+  }
+  __syncthreads();  // the gates are in LDS
+
+#pragma unroll 1
+  for (int s = 0; s < G; ++s) {
+    const int hv = g * G + s;
+    char *unit = unit_of(hv);
+    bf16 *E_hi = reinterpret_cast<bf16 *>(unit);
+    bf16 *E_lo = E_hi + D * kC;
+    bf16 *MT_hi = E_lo + D * kC;
+    bf16 *MT_lo = MT_hi + kC * kC;
+    if (s > 0) __syncthreads();  // every wave is done with the previous value head's M and K^T
+    // Abar of value head s from the Gram tiles (tiles above the diagonal are never read)
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      if (tj <= ti) {
+        const float gc = s_gam[s][16 * tj + lr];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = 16 * ti + 4 * lg + rr, c = 16 * tj + lr;
+          s_A[r][c] = (c < r) ? s_bb[s][r] * __expf(s_gam[s][r] - gc) * gk[tj][rr] : 0.0f;  // c < r: argument <= 0
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- C: L^-1 for L = I + Abar (unit lower triangular), fp32 ----
+    // Level 1: the four 16x16 diagonal blocks, right-looking substitution (wave 0:
+    // lane = block * 16 + column; after step m, x[m] is final and the updates of
+    // the rows below it are independent).  The blocks above the diagonal are never
+    // written: phase D, the only reader of those entries, masks them.
+    if (wave == 0) {
+      const int bk = lane / 16, c = lane % 16;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int m = 0; m < 15; ++m)
+#pragma unroll
+        for (int r = m + 1; r < 16; ++r) x[r] -= s_A[16 * bk + r][16 * bk + m] * x[m];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_L[16 * bk + r][16 * bk + c] = x[r];
+    }
+    __syncthreads();
+    // Level 2: [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1] on the two 32x32 diagonal
+    // blocks (wave 0: rows 0..31, wave 1: rows 32..63).
+    if (wave < 2) {
+      const int o = 32 * wave;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm16_f32(&s_A[o + 16][o], kLF, &s_L[o][o], kLF, acc, lr, lg);  // C A^-1
+      store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
+    }
+    __syncthreads();
+    if (wave < 2) {
+      const int o = 32 * wave;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm16_f32(&s_L[o + 16][o + 16], kLF, &s_Y[wave][0][0], 17, acc, lr, lg);  // B^-1 (C A^-1)
+      store_tile(&s_L[o + 16][o], kLF, acc, -1.0f, lr, lg);
+    }
+    __syncthreads();
+    // Level 3: the same identity with 32x32 blocks; wave w owns output tile (w/2, w%2).
+    {
+      const int yi = wave >> 1, yj = wave & 1;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      // Y = C A^-1, C = Abar[32:64, 0:32], A^-1 = L^-1[0:32, 0:32] (lower: k >= yj)
+      for (int k = yj; k < 2; ++k)
+        acc = mm16_f32(&s_A[32 + 16 * yi][16 * k], kLF, &s_L[16 * k][16 * yj], kLF, acc, lr, lg);
+      store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
+    }
+    __syncthreads();
+    {
+      const int xi = wave >> 1, xj = wave & 1;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      // X = -B^-1 Y, B^-1 = L^-1[32:64, 32:64] (lower: k <= xi)
+      for (int k = 0; k <= xi; ++k)
+        acc = mm16_f32(&s_L[32 + 16 * xi][32 + 16 * k], kLF, &s_Y[2 * k + xj][0][0], 17, acc, lr, lg);
+      store_tile(&s_L[32 + 16 * xi][16 * xj], kLF, acc, -1.0f, lr, lg);
+    }
+    __syncthreads();
+
+    // ---- D: T = L^-1 diag(b); MT = M T and E = K^T diag(D) T on MFMA ----
+    // Wave w owns rows j in [16w, 16w + 16) of T^T; its A operands are columns of T,
+    // read now, before L^-1's region is reused for M.
+    load_kt();
+    const int jrow = 16 * wave + lr;
+    const float bj = s_bb[s][jrow];
+    bf16x8 th[2], tl[2], dh[2], dl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t wth[4], wtl[4], wdh[4], wdl[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int sr = 8 * lg + 32 * ks + e;
+        // L^-1 is zero above its diagonal blocks (block row 2 ks + lg / 2 < block column wave)
+        const bool upper = wave > 2 * ks + (lg >> 1);
+        const float t0v = upper ? 0.0f : s_L[sr][jrow] * bj, t1v = upper ? 0.0f : s_L[sr + 1][jrow] * bj;
+        const Split2 ts = split_bf16_2(t0v, t1v), ds = split_bf16_2(s_dec[s][sr] * t0v, s_dec[s][sr + 1] * t1v);
+        wth[e / 2] = ts.hi;
+        wtl[e / 2] = ts.lo;
+        wdh[e / 2] = ds.hi;
+        wdl[e / 2] = ds.lo;
+      }
+      th[ks] = as_bf16x8(make_uint4(wth[0], wth[1], wth[2], wth[3]));
+      tl[ks] = as_bf16x8(make_uint4(wtl[0], wtl[1], wtl[2], wtl[3]));
+      dh[ks] = as_bf16x8(make_uint4(wdh[0], wdh[1], wdh[2], wdh[3]));
+      dl[ks] = as_bf16x8(make_uint4(wdl[0], wdl[1], wdl[2], wdl[3]));
+    }
+    __syncthreads();
+    // M of value head s (hi/lo) into R0, from the Gram tiles; the first part of K^T
+    // (rows past the chunk end zero: E must see exact zeros) into R1
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      const float gc = s_gam[s][16 * tj + lr];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int r = 16 * ti + 4 * lg + rr, c = 16 * tj + lr;
-        const float dec = __expf(s_gam[r] - gc);  // c <= r: the argument is <= 0
-        s_A[r][c] = (c < r) ? s_bb[r] * dec * ak[rr] : 0.0f;
-        mv[tj][rr] = (c <= r) ? dec * aq[rr] : 0.0f;
+        // M[r][c] = exp(gamma_r - gamma_c) (q_r . k_c) for c <= r (the argument is <= 0), else 0
+        const float mvv = (tj <= ti && c <= r) ? __expf(s_gam[s][r] - gc) * gq[tj][rr] : 0.0f;
+        bf16 hi, lo;
+        split_bf16(mvv, hi, lo);
+        s_M[0][r][c] = hi;
+        s_M[1][r][c] = lo;
       }
-    } else {  // above the diagonal: M is zero, Abar's tile is never read
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) mv[tj][rr] = 0.0f;
     }
-  }
-  __syncthreads();
-
-  // ---- C: L^-1 for L = I + Abar (unit lower triangular), fp32 ----
-  // Level 1: the four 16x16 diagonal blocks, right-looking substitution (wave 0:
-  // lane = block * 16 + column; after step m, x[m] is final and the updates of
-  // the rows below it are independent).  The blocks above the diagonal are never
-  // written: phase D, the only reader of those entries, masks them.
-  if (wave == 0) {
-    const int bk = lane / 16, c = lane % 16;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int m = 0; m < 15; ++m)
-#pragma unroll
-      for (int r = m + 1; r < 16; ++r) x[r] -= s_A[16 * bk + r][16 * bk + m] * x[m];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s_L[16 * bk + r][16 * bk + c] = x[r];
-  }
-  __syncthreads();
-  // Level 2: [A 0; C B]^-1 = [A^-1 0; -B^-1 C A^-1  B^-1] on the two 32x32 diagonal
-  // blocks (wave 0: rows 0..31, wave 1: rows 32..63).
-  if (wave < 2) {
-    const int o = 32 * wave;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm16_f32(&s_A[o + 16][o], kLF, &s_L[o][o], kLF, acc, lr, lg);  // C A^-1
-    store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
-  }
-  __syncthreads();
-  if (wave < 2) {
-    const int o = 32 * wave;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm16_f32(&s_L[o + 16][o + 16], kLF, &s_Y[wave][0][0], 17, acc, lr, lg);  // B^-1 (C A^-1)
-    store_tile(&s_L[o + 16][o], kLF, acc, -1.0f, lr, lg);
-  }
-  __syncthreads();
-  // Level 3: the same identity with 32x32 blocks; wave w owns output tile (w/2, w%2).
-  {
-    const int yi = wave >> 1, yj = wave & 1;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Y = C A^-1, C = Abar[32:64, 0:32], A^-1 = L^-1[0:32, 0:32] (lower: k >= yj)
-    for (int k = yj; k < 2; ++k)
-      acc = mm16_f32(&s_A[32 + 16 * yi][16 * k], kLF, &s_L[16 * k][16 * yj], kLF, acc, lr, lg);
-    store_tile(&s_Y[wave][0][0], 17, acc, 1.0f, lr, lg);
-  }
-  __syncthreads();
-  {
-    const int xi = wave >> 1, xj = wave & 1;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    // X = -B^-1 Y, B^-1 = L^-1[32:64, 32:64] (lower: k <= xi)
-    for (int k = 0; k <= xi; ++k)
-      acc = mm16_f32(&s_L[32 + 16 * xi][32 + 16 * k], kLF, &s_Y[2 * k + xj][0][0], 17, acc, lr, lg);
-    store_tile(&s_L[32 + 16 * xi][16 * xj], kLF, acc, -1.0f, lr, lg);
-  }
-  __syncthreads();
-
-  // ---- D: T = L^-1 diag(b); MT = M T and E = K^T diag(D) T on MFMA ----
-  // Wave w owns rows j in [16w, 16w + 16) of T^T; its A operands are columns of T,
-  // read now, before L^-1's region is reused for M.
-  if constexpr (SP) load_kt();
-  const int jrow = 16 * wave + lr;
-  const float bj = s_bb[jrow];
-  bf16x8 th[2], tl[2], dh[2], dl[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    uint32_t wth[4], wtl[4], wdh[4], wdl[4];
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int sr = 8 * lg + 32 * ks + e;
-      // L^-1 is zero above its diagonal blocks (block row 2 ks + lg / 2 < block column wave)
-      const bool upper = wave > 2 * ks + (lg >> 1);
-      const float t0v = upper ? 0.0f : s_L[sr][jrow] * bj, t1v = upper ? 0.0f : s_L[sr + 1][jrow] * bj;
-      const Split2 ts = split_bf16_2(t0v, t1v), ds = split_bf16_2(s_dec[sr] * t0v, s_dec[sr + 1] * t1v);
-      wth[e / 2] = ts.hi;
-      wtl[e / 2] = ts.lo;
-      wdh[e / 2] = ds.hi;
-      wdl[e / 2] = ds.lo;
-    }
-    th[ks] = as_bf16x8(make_uint4(wth[0], wth[1], wth[2], wth[3]));
-    tl[ks] = as_bf16x8(make_uint4(wtl[0], wtl[1], wtl[2], wtl[3]));
-    dh[ks] = as_bf16x8(make_uint4(wdh[0], wdh[1], wdh[2], wdh[3]));
-    dl[ks] = as_bf16x8(make_uint4(wdl[0], wdl[1], wdl[2], wdl[3]));
-  }
-  __syncthreads();
-  // M (hi/lo) into R0, the first part of K^T (rows past the chunk end zero: E must see
-  // exact zeros) into R1
-#pragma unroll
-  for (int tj = 0; tj < 4; ++tj)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      bf16 hi, lo;
-      split_bf16(mv[tj][rr], hi, lo);
-      s_M[0][16 * ti + 4 * lg + rr][16 * tj + lr] = hi;
-      s_M[1][16 * ti + 4 * lg + rr][16 * tj + lr] = lo;
-    }
-  {
-    const bool live = lane < L;
-#pragma unroll
-    for (int m = 0; m < NIG / NPASS; ++m)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        s_Kt[0][8 * (wave + 4 * m) + u][lane] = live ? kth[m][u] : (bf16)0.0f;
-        if (SP) s_Kt[NP - 1][8 * (wave + 4 * m) + u][lane] = live ? ktl[m][u] : (bf16)0.0f;
-      }
-  }
-  __syncthreads();
-  // The lane's results below are X[r0 + lr][16 wave + 4 lg + r], r = 0..3 (X = MT or E,
-  // r0 the tile's first row): four consecutive columns, one 8-byte word of the
-  // spine's fragment order (pfrag_off).
-  // MT^T[j][t] = sum_s T[s][j] M[t][s]; lane holds column t, rows j..j+3 -> MT[t][j..j+3]
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 mh = *reinterpret_cast<const bf16x8 *>(&s_M[0][16 * tt + lr][8 * lg + 32 * ks]);
-      const bf16x8 ml = *reinterpret_cast<const bf16x8 *>(&s_M[1][16 * tt + lr][8 * lg + 32 * ks]);
-      acc = mma<true, true>(acc, th[ks], tl[ks], mh, ml);
-    }
-    const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    const int fo = pfrag_off(16 * tt + lr, 16 * wave + 4 * lg);
-    store_split4(MT_hi + fo, MT_lo + fo, v);
-  }
-  // E^T[j][i] = sum_s D_s T[s][j] K[s][i]; lane holds column i, rows j..j+3 -> E[i][j..j+3]
-#pragma unroll
-  for (int part = 0; part < NPASS; ++part) {
-    if (part > 0) {  // K^T rows [D/NPASS part, D/NPASS (part + 1)), once every wave is done with the last part
-      __syncthreads();
+    {
       const bool live = lane < L;
 #pragma unroll
-      for (int m = part * (NIG / NPASS); m < (part + 1) * (NIG / NPASS); ++m)
+      for (int m = 0; m < NIG / NPASS; ++m)
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int row = 8 * (wave + 4 * m) + u - part * (D / NPASS);
-          s_Kt[0][row][lane] = live ? kth[m][u] : (bf16)0.0f;
-          if (SP) s_Kt[NP - 1][row][lane] = live ? ktl[m][u] : (bf16)0.0f;
+          s_Kt[0][8 * (wave + 4 * m) + u][lane] = live ? kth[m][u] : (bf16)0.0f;
+          if (SP) s_Kt[NP - 1][8 * (wave + 4 * m) + u][lane] = live ? ktl[m][u] : (bf16)0.0f;
         }
-      __syncthreads();
     }
+    __syncthreads();
+    // The lane's results below are X[r0 + lr][16 wave + 4 lg + r], r = 0..3 (X = MT or E,
+    // r0 the tile's first row): four consecutive columns, one 8-byte word of the
+    // spine's fragment order (pfrag_off).
+    // MT^T[j][t] = sum_s T[s][j] M[t][s]; lane holds column t, rows j..j+3 -> MT[t][j..j+3]
 #pragma unroll
-    for (int tp = 0; tp < NTP; ++tp) {
-      const int tix = part * NTP + tp;
+    for (int tt = 0; tt < 4; ++tt) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 khh = *reinterpret_cast<const bf16x8 *>(&s_Kt[0][16 * tp + lr][8 * lg + 32 * ks]);
-        const bf16x8 kll = SP ? *reinterpret_cast<const bf16x8 *>(&s_Kt[NP - 1][16 * tp + lr][8 * lg + 32 * ks])
-                              : zero8();
-        acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
+        const bf16x8 mh = *reinterpret_cast<const bf16x8 *>(&s_M[0][16 * tt + lr][8 * lg + 32 * ks]);
+        const bf16x8 ml = *reinterpret_cast<const bf16x8 *>(&s_M[1][16 * tt + lr][8 * lg + 32 * ks]);
+        acc = mma<true, true>(acc, th[ks], tl[ks], mh, ml);
       }
       const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-      const int fo = pfrag_off(16 * tix + lr, 16 * wave + 4 * lg);
-      store_split4(E_hi + fo, E_lo + fo, v);
+      const int fo = pfrag_off(16 * tt + lr, 16 * wave + 4 * lg);
+      store_split4(MT_hi + fo, MT_lo + fo, v);
+    }
+    // E^T[j][i] = sum_s D_s T[s][j] K[s][i]; lane holds column i, rows j..j+3 -> E[i][j..j+3]
+#pragma unroll
+    for (int part = 0; part < NPASS; ++part) {
+      if (part > 0) {  // K^T rows [D/NPASS part, D/NPASS (part + 1)), once every wave is done with the last part
+        __syncthreads();
+        const bool live = lane < L;
+#pragma unroll
+        for (int m = part * (NIG / NPASS); m < (part + 1) * (NIG / NPASS); ++m)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int row = 8 * (wave + 4 * m) + u - part * (D / NPASS);
+            s_Kt[0][row][lane] = live ? kth[m][u] : (bf16)0.0f;
+            if (SP) s_Kt[NP - 1][row][lane] = live ? ktl[m][u] : (bf16)0.0f;
+          }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int tp = 0; tp < NTP; ++tp) {
+        const int tix = part * NTP + tp;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 khh = *reinterpret_cast<const bf16x8 *>(&s_Kt[0][16 * tp + lr][8 * lg + 32 * ks]);
+          const bf16x8 kll = SP ? *reinterpret_cast<const bf16x8 *>(&s_Kt[NP - 1][16 * tp + lr][8 * lg + 32 * ks])
+                                : zero8();
+          acc = mma<true, SP>(acc, dh[ks], dl[ks], khh, kll);
+        }
+        const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+        const int fo = pfrag_off(16 * tix + lr, 16 * wave + 4 * lg);
+        store_split4(E_hi + fo, E_lo + fo, v);
+      }
     }
   }
 }
@@ -1043,7 +1048,7 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hv)), dim3(256), 0, stream, p, tb, units, kq);
+  hipLaunchKernelGGL((prep_kernel<D, TY>), dim3((unsigned)(NC * p.geo.Hk)), dim3(256), 0, stream, p, tb, units, kq);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 16-column blocks while that is what it takes to give every CU a workgroup
