@@ -52,7 +52,8 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitLaunch p, int64_t n4,
     const gptr<const floatx4> src = to_global(static_cast<const floatx4 *>(p.tables[na * kTableSeqs + i]));
     const gptr<floatx4> dst = to_global(static_cast<floatx4 *>(p.tables[i]));
     const int64_t idx = (int64_t)blockIdx.x * kCommitTile + threadIdx.x;
-    if (idx < n4) dst[idx] = src[idx];
+    // non-temporal, as the other state streams (64 accepted states: 48.5 -> 42.5 us by events)
+    if (idx < n4) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[idx]), &dst[idx]);
   } else {
     advance_ring<TE>(p.geo, p.conv_state, p.x, p.cu, i, na, (int)blockIdx.x - ntiles);
   }

@@ -48,25 +48,40 @@ typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 
 // 4 consecutive state elements of either storage type: raw load, widening, and
 // the value a 4-vector takes once stored (binary16: rounded to nearest even).
+// Loads and store() carry the non-temporal hint: a state is read once and written
+// once per call, and streaming it past the caches' normal allocation moves it
+// faster (cache-cold batched decode 109 -> 97.5 us, fold 64 -> 55 us on one
+// MI355X).  store_kept() is the plain store, for the verify that records a state
+// after every row: with the hint its stores ran 6 % slower.
 template <typename TS>
 struct StateIO;
 template <>
 struct StateIO<float> {
   typedef floatx4 raw;
-  static __device__ __forceinline__ raw load(gptr<const float> p) { return *reinterpret_cast<gptr<const floatx4>>(p); }
+  static __device__ __forceinline__ raw load(gptr<const float> p) {
+    return __builtin_nontemporal_load(reinterpret_cast<gptr<const floatx4>>(p));
+  }
   static __device__ __forceinline__ floatx4 widen(raw r) { return r; }
   static __device__ __forceinline__ floatx4 as_stored(floatx4 v) { return v; }
-  static __device__ __forceinline__ void store(gptr<float> p, floatx4 v) { *reinterpret_cast<gptr<floatx4>>(p) = v; }
+  static __device__ __forceinline__ void store(gptr<float> p, floatx4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<gptr<floatx4>>(p));
+  }
+  static __device__ __forceinline__ void store_kept(gptr<float> p, floatx4 v) { *reinterpret_cast<gptr<floatx4>>(p) = v; }
 };
 template <>
 struct StateIO<_Float16> {
   typedef halfx4 raw;
-  static __device__ __forceinline__ raw load(gptr<const _Float16> p) { return *reinterpret_cast<gptr<const halfx4>>(p); }
+  static __device__ __forceinline__ raw load(gptr<const _Float16> p) {
+    return __builtin_nontemporal_load(reinterpret_cast<gptr<const halfx4>>(p));
+  }
   static __device__ __forceinline__ floatx4 widen(raw r) { return __builtin_convertvector(r, floatx4); }
   static __device__ __forceinline__ floatx4 as_stored(floatx4 v) {
     return __builtin_convertvector(__builtin_convertvector(v, halfx4), floatx4);
   }
   static __device__ __forceinline__ void store(gptr<_Float16> p, floatx4 v) {
+    __builtin_nontemporal_store(__builtin_convertvector(v, halfx4), reinterpret_cast<gptr<halfx4>>(p));
+  }
+  static __device__ __forceinline__ void store_kept(gptr<_Float16> p, floatx4 v) {
     *reinterpret_cast<gptr<halfx4>>(p) = __builtin_convertvector(v, halfx4);
   }
 };
@@ -463,7 +478,10 @@ void recurrent_kernel(RecurrentLaunch p) {
       const floatx4 nv = StateIO<TS>::as_stored(rank1_update(st_reg[rr], av, kr[rr], u));
       st_reg[rr] = nv;
       if (store_now) {
-        StateIO<TS>::store(dst + (size_t)state_row<D>(rg, rr) * D + 4 * cq, nv);
+        if constexpr (kStoresEveryRow)
+          StateIO<TS>::store_kept(dst + (size_t)state_row<D>(rg, rr) * D + 4 * cq, nv);
+        else
+          StateIO<TS>::store(dst + (size_t)state_row<D>(rg, rr) * D + 4 * cq, nv);
         // binary16: issue each narrowed row now rather than holding them all
         if constexpr (sizeof(TS) == 2 && kStoresEveryRow) __builtin_amdgcn_sched_barrier(0);
       }
