@@ -48,16 +48,16 @@ VERIFY_SETS = 2                         # state sets the verify/commit alternate
 # rocprofv3 counter runs of `bench.py --steps 1 --warmup 0 --no-cpu-baseline`
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, mean of the step's decode dispatches),
 # each scaled by what the same counter reads for one 1 GiB device copy (`bench.py
-# --copy-calib`: FETCH_SIZE 524301.9 KiB, WRITE_SIZE 1048576.0 KiB per copy).  The
+# --copy-calib`: FETCH_SIZE 524302.1 KiB, WRITE_SIZE 1048576.0 KiB per copy).  The
 # figures hold for the kernel sources they were taken on only (SHA-256 over the files
 # below); for any other source the traffic is reported as unknown.
 DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "dae8b2f586478d4465e797127d0d2c02c8814592c7543437e22578904b1a8a75",
-    "fetch_kib": 136067.1, "write_kib": 269312.0,
-    "fetch_scale": 1048576.0 / 524301.9, "write_scale": 1048576.0 / 1048576.0,
+    "sha256": "7a7fd8479075b9c75f1c6da924af062e2199178b0a2b571227d02a00b836bfc2",
+    "fetch_kib": 135901.0, "write_kib": 269524.6,
+    "fetch_scale": 1048576.0 / 524302.1, "write_scale": 1048576.0 / 1048576.0,
 }
 
 
