@@ -939,10 +939,14 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     const size_t ostride = (size_t)Hv * D;
     const int ocol = h * D + CB * cb + lr;
     const uint32_t ooff = (uint32_t)((8 * lg * ostride + ocol) * sizeof(TO));
-    uint4 qf[2][KS][NP];  // Q fragments of the tile, all k-steps, hi (, lo); chunk parity
-    uint4 mf[2][2][2];    // MT fragments: chunk parity, token k-step, hi / lo
-    floatx4 go[2];        // Gam of the tile's tokens; chunk parity
-    Raw8<TY> vr[2];       // V of the tile for the chain waves: operand row vm, 8 columns from vc
+    // NB buffers, filled NB chunks ahead: two with bf16 activations; one with fp32
+    // activations, whose hi/lo fragments would otherwise hold the kernel to one
+    // workgroup per CU
+    constexpr int NB = SP ? 1 : 2;
+    uint4 qf[NB][KS][NP];  // Q fragments of the tile, all k-steps, hi (, lo); chunk parity
+    uint4 mf[NB][2][2];    // MT fragments: chunk parity, token k-step, hi / lo
+    floatx4 go[NB];        // Gam of the tile's tokens; chunk parity
+    Raw8<TY> vr[NB];       // V of the tile for the chain waves: operand row vm, 8 columns from vc
     // V of the tile's 16 rows x CB columns, 8 columns per lane (lanes past 2 CB
     // rows' worth -- 16-column blocks -- repeat the first half: same data)
     constexpr int LPR = CB / 8;  // lanes per row
@@ -955,15 +959,15 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
-          qf[PAR][s][pl] = bload16(rq, 2 * (uint32_t)((NP + pl) * kC * D + frag_off(tt, s, KS, lane)));
-      bload(vr[PAR], tile_rows(c, tt), vof);
-      go[PAR] = bloadf4(make_rsrc(unit_of(c), unit_bytes(D)), kGamOff + 4 * (uint32_t)row_of(tt, 4 * lg));
+          qf[PAR % NB][s][pl] = bload16(rq, 2 * (uint32_t)((NP + pl) * kC * D + frag_off(tt, s, KS, lane)));
+      bload(vr[PAR % NB], tile_rows(c, tt), vof);
+      go[PAR % NB] = bloadf4(make_rsrc(unit_of(c), unit_bytes(D)), kGamOff + 4 * (uint32_t)row_of(tt, 4 * lg));
     };
     // the chunk's V (in the activation dtype) and Gam to LDS for the chain waves
     auto put_vg = [&](auto par) {
       constexpr int PAR = decltype(par)::value;
-      store_raw(&s_V[tt][vm][vc], vr[PAR]);
-      s_G[tt][lane] = go[PAR];
+      store_raw(&s_V[tt][vm][vc], vr[PAR % NB]);
+      s_G[tt][lane] = go[PAR % NB];
     };
     auto fetch_mt = [&](auto par, int c) {
       constexpr int PAR = decltype(par)::value;
@@ -972,7 +976,7 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int hl = 0; hl < 2; ++hl)
-          mf[PAR][s][hl] = bload16(ru, 2 * (uint32_t)(2 * D * kC + hl * kC * kC + frag_off(tt, s, 2, lane)));
+          mf[PAR % NB][s][hl] = bload16(ru, 2 * (uint32_t)(2 * D * kC + hl * kC * kC + frag_off(tt, s, 2, lane)));
     };
     auto out_chunk = [&](int c, auto par) {
       constexpr int PAR = decltype(par)::value;
@@ -982,7 +986,7 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       for (int ct = 0; ct < NC; ++ct) O[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 qh = as_bf16x8(qf[PAR][s][0]), ql = as_bf16x8(qf[PAR][s][NP - 1]);
+        const bf16x8 qh = as_bf16x8(qf[PAR % NB][s][0]), ql = as_bf16x8(qf[PAR % NB][s][NP - 1]);
 #pragma unroll
         for (int ct = 0; ct < NC; ++ct) {
           const bf16x8 hh = s_H[s][0][ct][lane], hl = s_H[s][1][ct][lane];
@@ -992,8 +996,8 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
         }
       }
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct) O[ct] *= go[PAR];
-      fetch_q(par, min(c + 2, nch - 1));  // this chunk's Q and Gam are consumed
+      for (int ct = 0; ct < NC; ++ct) O[ct] *= go[PAR % NB];
+      fetch_q(par, min(c + NB, nch - 1));  // this chunk's Q and Gam are consumed
       __syncthreads();  // barrier 2: X of chunk c is in LDS
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -1001,9 +1005,9 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
         for (int ct = 0; ct < NC; ++ct) {
           const bf16x8 xh = *reinterpret_cast<const bf16x8 *>(&s_X[s][0][ct][lane][0]);
           const bf16x8 xl = *reinterpret_cast<const bf16x8 *>(&s_X[s][1][ct][lane][0]);
-          O[ct] = mfma16(as_bf16x8(mf[PAR][s][0]), xh, O[ct]);
-          O[ct] = mfma16(as_bf16x8(mf[PAR][s][0]), xl, O[ct]);
-          O[ct] = mfma16(as_bf16x8(mf[PAR][s][1]), xh, O[ct]);
+          O[ct] = mfma16(as_bf16x8(mf[PAR % NB][s][0]), xh, O[ct]);
+          O[ct] = mfma16(as_bf16x8(mf[PAR % NB][s][0]), xl, O[ct]);
+          O[ct] = mfma16(as_bf16x8(mf[PAR % NB][s][1]), xh, O[ct]);
         }
       // stores through the tile's descriptor over o: rows past the chunk's end are dropped
       const int r0 = 32 * (tt >> 1) + 4 * (tt & 1);
@@ -1014,15 +1018,18 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           bstore(ro, ooff + (uint32_t)((r * ostride + 16 * ct) * sizeof(TO)), (TO)(p.scale * O[ct][r]));
-      fetch_mt(par, min(c + 2, nch - 1));
+      fetch_mt(par, min(c + NB, nch - 1));
       // next chunk's V and Gam for the chain waves (read after barrier 1; the chain
       // waves finished reading this chunk's before barrier 2)
-      if (PAR == 0) put_vg(P1()); else put_vg(P0());
+      // (one buffer: fetch_q above has just brought the next chunk's into it)
+      if (NB == 1 || PAR == 1) put_vg(P0()); else put_vg(P1());
     };
     fetch_q(P0(), 0);
     fetch_mt(P0(), 0);
-    fetch_q(P1(), min(1, nch - 1));
-    fetch_mt(P1(), min(1, nch - 1));
+    if constexpr (NB == 2) {
+      fetch_q(P1(), min(1, nch - 1));
+      fetch_mt(P1(), min(1, nch - 1));
+    }
     put_vg(P0());
 #pragma unroll 1
     for (int c = 0; c < nch; c += 2) {
