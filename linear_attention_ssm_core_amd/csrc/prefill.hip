@@ -26,12 +26,12 @@
 //      sequence; every chunk's entry filled in parallel) and a longest-first
 //      sequence order.  With one sequence the list is implicit (chunk c = rows
 //      64 c ..) and this launch is skipped.
-//   2. prep_kernel, one workgroup per (chunk, value head), all chunks in parallel: K K^T
-//      and Q K^T on bf16 MFMA, the 64x64 UT solve in fp32 (16x16 blocks: the four
-//      diagonal blocks by substitution, the off-diagonal blocks by block products),
-//      then E and MT on MFMA.  E and MT go to the workspace as bf16 hi/lo pairs in MFMA
-//      fragment order, so the next kernel loads each fragment as one contiguous 1 KiB
-//      block.
+//   2. prep_kernel, one workgroup per (chunk, key head), all chunks in parallel: K K^T
+//      and Q K^T on bf16 MFMA once for the key head's value heads, then per value
+//      head the 64x64 UT solve in fp32 (16x16 blocks: the four diagonal blocks by
+//      substitution, the off-diagonal blocks by block products) and E and MT on
+//      MFMA.  E and MT go to the workspace as bf16 hi/lo pairs in MFMA fragment
+//      order, so the next kernel loads each fragment as one contiguous 1 KiB block.
 //   3. spine_kernel, one workgroup per (sequence, value head, 16- or 32-column block
 //      of d_v): the serial pass over the chunks.  d_k / 32 "chain" waves keep the
 //      state block in MFMA accumulators (one d_k k-step each) and carry
@@ -258,6 +258,8 @@ struct PrepLds {
   static constexpr size_t r1 = (size_t)kC * kLF * 4 > kt ? (size_t)kC * kLF * 4 : kt;
 };
 
+// Held to three waves per SIMD (<= 168 VGPRs): with the LDS above, three workgroups
+// then share a CU.
 template <int D, typename TY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prep_kernel(PrefillLaunch p, Tables tb, char *units, char *kq) {
   constexpr bool SP = std::is_same<TY, float>::value;
