@@ -722,10 +722,12 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
   __shared__ bf16x8 s_H[KS][2][NC][kWave];     // h as B operands: k-step, hi/lo, column tile
   __shared__ uint2 s_X[2][2][NC][kWave][2];    // X as B operands: token k-step, hi/lo, column tile, lane, tile parity
   // V and Gam of the next chunk, from the output waves (each loads its token tile's
-  // V rows with one 16-byte access per lane), for the chain waves; written before
-  // barrier 1, read before barrier 2.  V rows in operand-row order m of the tile.
+  // V rows, 16 bytes per lane, and the chunk's 64 Gam, 4 bytes per lane), for every
+  // wave; written before barrier 1, read before barrier 2.  V rows in operand-row
+  // order m of the tile; Gam by token, so a lane's 4 rows row_of(tt, 4 lg + r) are
+  // 4 consecutive values.
   __shared__ __align__(16) TY s_V[4][16][CB];
-  __shared__ floatx4 s_G[4][kWave];           // Gam of token row_of(tt, 4 lg + r)
+  __shared__ __align__(16) float s_G[kC];
 
   const TY *y = static_cast<const TY *>(p.y);
   auto unit_of = [&](int c) { return units + ((size_t)(c_first + c) * Hv + h) * unit_bytes(D); };
@@ -860,9 +862,9 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       }
       fetch_k(cn);
       __syncthreads();  // barrier 1
-      // Gam_63 of this chunk: row 63 = row_of(3, 15), held by lanes 48.. of tile 3 in
-      // component 3 (read before barrier 2: the output waves overwrite s_G after it)
-      const float gC = s_G[3][48][3];
+      // Gam_63 of this chunk (read before barrier 2: the output waves overwrite s_G
+      // after it)
+      const float gC = s_G[kC - 1];
       // X of the own token tiles: partials summed in wave order (the own one read
       // back too: picking it out of pp by the wave-dependent tile index would put pp
       // in scratch memory), then V - Gam P, split into this wave's half of the token
@@ -880,7 +882,7 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
             for (int w2 = 1; w2 < KS; ++w2) P += s_P[w2][tt][ct][lane];
           }
-          const floatx4 gam = s_G[tt][lane];
+          const floatx4 gam = *reinterpret_cast<const floatx4 *>(&s_G[row_of(tt, 4 * lg)]);
           float X[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) X[r] = ld(&s_V[tt][4 * lg + r][0], 16 * ct + lr) - gam[r] * P[r];
@@ -947,13 +949,18 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     constexpr int NB = SP ? 1 : 2;
     uint4 qf[NB][KS][NP];  // Q fragments of the tile, all k-steps, hi (, lo); chunk parity
     uint4 mf[NB][2][2];    // MT fragments: chunk parity, token k-step, hi / lo
-    floatx4 go[NB];        // Gam of the tile's tokens; chunk parity
+    float go[NB];          // Gam of token `lane` of the chunk; chunk parity
     Raw8<TY> vr[NB];       // V of the tile for the chain waves: operand row vm, 8 columns from vc
-    // V of the tile's 16 rows x CB columns, 8 columns per lane (lanes past 2 CB
-    // rows' worth -- 16-column blocks -- repeat the first half: same data)
+    // V of the tile's 16 rows x CB columns, 8 columns per lane.  With 16-column blocks
+    // that takes half the wave: the other lanes read past the descriptor's extent
+    // (zeros, no memory access) and write nothing.
     constexpr int LPR = CB / 8;  // lanes per row
     const int vm = (lane / LPR) & 15, vc = 8 * (lane % LPR);
-    const uint32_t vof = ((8 * (vm >> 2) + (vm & 3)) * CD + 2 * Hk * D + h * D + CB * cb + vc) * (uint32_t)sizeof(TY);
+    const bool vlane = lane < 16 * LPR;
+    const uint32_t vof = vlane ? ((8 * (vm >> 2) + (vm & 3)) * CD + 2 * Hk * D + h * D + CB * cb + vc) * (uint32_t)sizeof(TY)
+                               : 0x7fff0000u;
+    // the token rows of this wave's tile: the Gam it writes to LDS
+    const bool grow = tt == 2 * (lane >> 5) + ((lane >> 2) & 1);
     auto fetch_q = [&](auto par, int c) {
       constexpr int PAR = decltype(par)::value;
       const Rsrc rq = kq_of(c);
@@ -963,13 +970,14 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
         for (int pl = 0; pl < NP; ++pl)
           qf[PAR % NB][s][pl] = bload16(rq, 2 * (uint32_t)((NP + pl) * kC * D + frag_off(tt, s, KS, lane)));
       bload(vr[PAR % NB], tile_rows(c, tt), vof);
-      go[PAR % NB] = bloadf4(make_rsrc(unit_of(c), unit_bytes(D)), kGamOff + 4 * (uint32_t)row_of(tt, 4 * lg));
+      go[PAR % NB] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(unit_of(c), unit_bytes(D)), (int)(kGamOff + 4 * lane), 0, 0));
     };
     // the chunk's V (in the activation dtype) and Gam to LDS for the chain waves
     auto put_vg = [&](auto par) {
       constexpr int PAR = decltype(par)::value;
-      store_raw(&s_V[tt][vm][vc], vr[PAR % NB]);
-      s_G[tt][lane] = go[PAR % NB];
+      if (vlane) store_raw(&s_V[tt][vm][vc], vr[PAR % NB]);
+      if (grow) s_G[lane] = go[PAR % NB];
     };
     auto fetch_mt = [&](auto par, int c) {
       constexpr int PAR = decltype(par)::value;
@@ -997,9 +1005,12 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
           if (SP) O[ct] = mfma16(ql, hh, O[ct]);
         }
       }
+      {
+        const floatx4 gam = *reinterpret_cast<const floatx4 *>(&s_G[row_of(tt, 4 * lg)]);
 #pragma unroll
-      for (int ct = 0; ct < NC; ++ct) O[ct] *= go[PAR % NB];
-      fetch_q(par, min(c + NB, nch - 1));  // this chunk's Q and Gam are consumed
+        for (int ct = 0; ct < NC; ++ct) O[ct] *= gam;
+      }
+      fetch_q(par, min(c + NB, nch - 1));  // this chunk's Q is consumed
       __syncthreads();  // barrier 2: X of chunk c is in LDS
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -1033,12 +1044,16 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
       fetch_mt(P1(), min(1, nch - 1));
     }
     put_vg(P0());
+    // pairs of chunks, then an odd last chunk after the loop: no exit from the middle
+    // of the body (that exit's merge of scalar values made the compiler read a
+    // register still being loaded, i.e. wait for the chunk's prefetch)
+    int c = 0;
 #pragma unroll 1
-    for (int c = 0; c < nch; c += 2) {
+    for (; c + 1 < nch; c += 2) {
       out_chunk(c, P0());
-      if (c + 1 >= nch) break;
       out_chunk(c + 1, P1());
     }
+    if (c < nch) out_chunk(c, P0());
   }
 }
 
