@@ -340,17 +340,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) frag8(krow + 32 * ks, kh[slot][ks], kl[slot][ks]);
   };
-  {
+  if constexpr (!SP) {
+    // bf16 activations: the chunk's Q and K rows go to LDS once (R0 and R1 are free
+    // until the solves), 16 bytes per thread and load, and every wave reads its MFMA
+    // operands there -- a quarter of the global loads of each wave fetching all the K
+    // tiles it multiplies.  Row stride D + 8 elements: the 16 rows of an operand read
+    // fall on distinct banks.
+    constexpr int kRS = D + 8;
+    constexpr int PER = kC * D / 8 / 256;  // 16-byte pieces per thread and matrix
+    static_assert((size_t)kC * kRS * 2 <= LDS::r0 && (size_t)kC * kRS * 2 <= LDS::r1, "staged rows fit R0 and R1");
+    bf16 *sq = reinterpret_cast<bf16 *>(s_r0), *sk = reinterpret_cast<bf16 *>(s_r1);
+    uint4 rq[PER], rk[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = tid + 256 * q, row = idx / (D / 8), cc = 8 * (idx % (D / 8));
+      rq[q] = *reinterpret_cast<const uint4 *>(Qb + (size_t)min(row, L - 1) * CD + cc);
+      rk[q] = *reinterpret_cast<const uint4 *>(Kb + (size_t)min(row, L - 1) * CD + cc);
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = tid + 256 * q, row = idx / (D / 8), cc = 8 * (idx % (D / 8));
+      *reinterpret_cast<uint4 *>(sq + row * kRS + cc) = rq[q];
+      *reinterpret_cast<uint4 *>(sk + row * kRS + cc) = rk[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qh[ks] = *reinterpret_cast<const bf16x8 *>(sq + (16 * ti + lr) * kRS + 32 * ks + 8 * lg);
+      kih[ks] = *reinterpret_cast<const bf16x8 *>(sk + (16 * ti + lr) * kRS + 32 * ks + 8 * lg);
+      ql[ks] = kil[ks] = zero8();
+    }
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kh[tj][ks] = *reinterpret_cast<const bf16x8 *>(sk + (16 * tj + lr) * kRS + 32 * ks + 8 * lg);
+        kl[tj][ks] = zero8();
+      }
+  } else {
     const TY *qrow = Qb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
     const TY *kirow = Kb + (size_t)min(16 * ti + lr, L - 1) * CD + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       frag8(qrow + 32 * ks, qh[ks], ql[ks]);
       frag8(kirow + 32 * ks, kih[ks], kil[ks]);
-    }
-    if constexpr (!SP) {
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) load_ktile(tj, tj);
     }
   }
   // The chunk's K and Q rows of tile ti for the spine: natural row r = 16 ti + lr is
