@@ -546,6 +546,8 @@ def main():
     pre_ms = np.mean(_pair_ms(ev["p1"], ev["p2"]))
     norm_ms = np.mean(_pair_ms(ev["p2"], ev["p3"]))
     dec_ms = np.array(_pair_ms(ev["d0"], ev["d1"])) / w.d_steps  # mean launch duration, per step
+    print("bench: decode us per launch, step by step: " + " ".join("%.1f" % (1e3 * x) for x in dec_ms),
+          file=sys.stderr, flush=True)
     ver_ms = np.mean(_pair_ms(ev["v0"], ev["v1"]))
     com_ms = np.mean(_pair_ms(ev["v1"], ev["v2"]))
 
