@@ -56,7 +56,7 @@ def _wy_form(dims, state):
 @pytest.mark.parametrize("case,state", [("config3", "f32"), ("config3", "f16"), ("tiny_fp32", "f32"),
                                         ("edge_k", "f32"), ("n128_k1", "f32"), ("d64_g4", "f16"),
                                         ("d64_g4", "f32"), ("extreme_raw_gates", "f32"), ("g1_f32act", "f32"),
-                                        ("g4_d128_k3", "f32"), ("repeat_keys", "f32")])
+                                        ("g4_d128_k3", "f32"), ("k2_d128", "f32"), ("repeat_keys", "f32")])
 def test_woa_verify_and_fold(case, state):
     """Outputs and stash against the oracle; the fold of the accepted rows against
     the oracle and against the state the write-all verify records after the same
@@ -99,6 +99,9 @@ def test_woa_verify_and_fold(case, state):
     elif case == "g1_f32act":  # one value head per key head, fp32 activations
         d = W.verify_inputs(3118, 5, W.Dims(Hk=4, Hv=4, dk=128, dv=128, K=4), act="f32", ks=[16, 3, 11, 1, 8])
         sample = np.arange(5)
+    elif case == "k2_d128":  # a 2-tap conv: one conv-state row, read by every lane of a quad
+        d = W.verify_inputs(3123, 4, W.Dims(Hk=4, Hv=8, dk=128, dv=128, K=2), act="bf16", ks=[16, 5, 2, 9])
+        sample = np.arange(4)
     elif case == "g4_d128_k3":  # four value heads per key head at d = 128, a 3-tap conv
         d = W.verify_inputs(3119, 5, W.Dims(Hk=2, Hv=8, dk=128, dv=128, K=3), act="bf16", ks=[7, 16, 2, 12, 5])
         sample = np.arange(5)
