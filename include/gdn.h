@@ -65,6 +65,12 @@
  *     the activation dtype.  The norm gate is SiLU(z), or sigmoid(z) with
  *     gdn_options.norm_gate = GDN_NORM_GATE_SIGMOID (a gdn_norm_sigmoid model,
  *     doc comment of gated_rms_norm_f32_strided_k on the layer_struct.rs page).
+ *   - Alignment: every buffer passed directly in an argument struct starts on a
+ *     16-byte boundary (hipMalloc and framework allocations do; a view into the
+ *     middle of one may not): the kernels move rows, outputs and the stash in 8- and
+ *     16-byte vectors.  A misaligned one makes the call return GDN_ERR_INVALID_ARG.
+ *     The per-sequence state and conv-state buffers reached through the pointer
+ *     arrays must be 16-byte aligned too; the library cannot check those.
  *   - Errors: any status other than GDN_OK except GDN_ERR_HIP means nothing was
  *     launched.  GDN_ERR_HIP reports a launch failure (hipGetLastError).
  *   - Calls on one stream are ordered; state buffers must not be shared by calls

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <initializer_list>
 
 #include "internal.h"
 
@@ -71,6 +72,13 @@ int stash_row_floats(const Geometry &g) { return (g.Hk * g.D + g.Hv * g.D + g.Hv
 
 bool finite(float v) { return std::isfinite(v); }
 bool eps_ok(float v) { return std::isfinite(v) && v >= 0.0f; }
+// Buffers the kernels move in 8- and 16-byte vectors must start on a 16-byte boundary
+// (hipMalloc and framework allocations do; a view into the middle of one may not).
+bool aligned16(std::initializer_list<const void *> ps) {
+  for (const void *q : ps)
+    if (reinterpret_cast<uintptr_t>(q) & 15) return false;
+  return true;
+}
 
 gdn_status hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
@@ -140,6 +148,7 @@ gdn_status gdn_conv_l2norm(const gdn_conv_args *a, void *stream) {
     return GDN_ERR_INVALID_ARG;
   if (a->total_tokens > 0 && (a->x == nullptr || a->y == nullptr)) return GDN_ERR_INVALID_ARG;
   if (a->x != nullptr && a->x == a->y) return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x, a->y, a->conv_w})) return GDN_ERR_INVALID_ARG;
   if (a->num_seqs > 65535) return GDN_ERR_INVALID_ARG;
   p.n = a->num_seqs;
   p.T = a->total_tokens;
@@ -166,6 +175,7 @@ gdn_status gdn_decode_batched(const gdn_decode_args *a, void *stream) {
        a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
   if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x, a->conv_w, a->z, a->norm_w, a->out})) return GDN_ERR_INVALID_ARG;
   Opts o;
   s = check_opts(a->opt, true, true, true, &o);
   if (s != GDN_OK) return s;
@@ -203,6 +213,7 @@ gdn_status gdn_verify_multi(const gdn_verify_args *a, void *stream) {
        a->a == nullptr || a->b == nullptr || a->wy_tables == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
   if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x, a->conv_w, a->z, a->norm_w, a->out})) return GDN_ERR_INVALID_ARG;
   Opts o;
   s = check_opts(a->opt, true, true, true, &o);
   if (s != GDN_OK) return s;
@@ -235,6 +246,7 @@ gdn_status gdn_verify_commit(const gdn_commit_args *a, void *stream) {
   if (a->num_seqs > 0 && (a->cu_ks == nullptr || a->n_accepted == nullptr || a->wy_tables == nullptr ||
                           a->x == nullptr || a->conv_state == nullptr))
     return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x})) return GDN_ERR_INVALID_ARG;
   Opts o;
   s = check_opts(a->opt, true, false, false, &o);
   if (s != GDN_OK) return s;
@@ -260,6 +272,7 @@ gdn_status gdn_gated_rmsnorm(const gdn_norm_args *a, void *stream) {
   if (a->total_tokens * d.num_v_heads > ((int64_t)1 << 33)) return GDN_ERR_INVALID_ARG;
   if (a->total_tokens > 0 && (a->o == nullptr || a->z == nullptr || a->norm_w == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->o, a->z, a->norm_w, a->out})) return GDN_ERR_INVALID_ARG;
   Opts o;
   gdn_status s = check_opts(a->opt, false, false, true, &o);
   if (s != GDN_OK) return s;
@@ -307,6 +320,7 @@ gdn_status check_prefill(const gdn_prefill_args *a, PrefillPlan *plan) {
   if (!plan->fused_front && T > 0 && a->y == nullptr) return GDN_ERR_INVALID_ARG;
   if (plan->epilogue && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
   if (n > 65535) return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->y, a->x, a->conv_w, a->z, a->norm_w, a->out, a->workspace})) return GDN_ERR_INVALID_ARG;
   return GDN_OK;
 }
 
@@ -428,6 +442,7 @@ gdn_status gdn_verify_woa(const gdn_woa_args *a, void *stream) {
        a->a == nullptr || a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
   if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x, a->conv_w, a->z, a->norm_w, a->out, a->stash})) return GDN_ERR_INVALID_ARG;
   Opts o;
   s = check_opts(a->opt, true, true, true, &o);
   if (s != GDN_OK) return s;
@@ -463,6 +478,7 @@ gdn_status gdn_fold_accepted(const gdn_fold_args *a, void *stream) {
   if (a->num_seqs > 0 && (a->cu_ks == nullptr || a->n_accepted == nullptr || a->h_state == nullptr ||
                           a->x == nullptr || a->conv_state == nullptr))
     return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x, a->stash})) return GDN_ERR_INVALID_ARG;
   Opts o;
   s = check_opts(a->opt, true, false, false, &o);
   if (s != GDN_OK) return s;
@@ -495,6 +511,7 @@ gdn_status gdn_decode_tokens(const gdn_tokens_args *a, void *stream) {
        a->a == nullptr || a->b == nullptr || a->h_state == nullptr || a->out == nullptr))
     return GDN_ERR_INVALID_ARG;
   if (a->z != nullptr && a->norm_w == nullptr) return GDN_ERR_INVALID_ARG;
+  if (!aligned16({a->x, a->conv_w, a->z, a->norm_w, a->out})) return GDN_ERR_INVALID_ARG;
   Opts o;
   s = check_opts(a->opt, true, true, true, &o);
   if (s != GDN_OK) return s;

@@ -307,3 +307,24 @@ def test_tokens_validation():
     assert _tokens(cu_tokens=None) == B.GDN_ERR_INVALID_ARG
     assert _tokens(z=FAKE) == B.GDN_ERR_INVALID_ARG
     assert _tokens(num_seqs=0, total_rows=0) == B.GDN_OK
+
+
+def test_misaligned_buffers_are_refused():
+    # buffers passed directly in the argument structs start on a 16-byte boundary
+    # (the kernels move them in 8- and 16-byte vectors); the check precedes any launch
+    bad = FAKE + 8
+    L = B.library()
+    assert _decode(x=bad) == B.GDN_ERR_INVALID_ARG
+    assert _decode(out=bad) == B.GDN_ERR_INVALID_ARG
+    assert _verify(conv_w=bad) == B.GDN_ERR_INVALID_ARG
+    assert _commit(x=bad) == B.GDN_ERR_INVALID_ARG
+    assert _conv(y=FAKE + 72) == B.GDN_ERR_INVALID_ARG
+    assert _norm(o=bad) == B.GDN_ERR_INVALID_ARG
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(out=bad)), None) == B.GDN_ERR_INVALID_ARG
+    need = _ws(_prefill_args())[1]
+    assert L.gdn_prefill_chunked(ctypes.byref(_prefill_args(workspace=bad, workspace_bytes=need)),
+                                 None) == B.GDN_ERR_INVALID_ARG
+    stash = 576 * (16 * 128 + 32 * 128 + 32) * 4
+    assert L.gdn_verify_woa(ctypes.byref(_woa_args(stash=bad, stash_bytes=stash)), None) == B.GDN_ERR_INVALID_ARG
+    assert _fold(stash=bad) == B.GDN_ERR_INVALID_ARG
+    assert _tokens(x=bad) == B.GDN_ERR_INVALID_ARG
