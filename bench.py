@@ -55,7 +55,7 @@ DECODE_TRAFFIC = {
     "sources": ["linear_attention_ssm_core_amd/csrc/recurrent_kernel.h",
                 "linear_attention_ssm_core_amd/csrc/recurrent_decode.hip",
                 "linear_attention_ssm_core_amd/csrc/common.h", "linear_attention_ssm_core_amd/csrc/internal.h"],
-    "sha256": "7a7fd8479075b9c75f1c6da924af062e2199178b0a2b571227d02a00b836bfc2",
+    "sha256": "a4dfcdce4b6656176b1d681c1a592f665d4198cf8b425aa59b5de7f61adc618e",
     "fetch_kib": 135901.0, "write_kib": 269524.6,
     "fetch_scale": 1048576.0 / 524302.1, "write_scale": 1048576.0 / 1048576.0,
 }

@@ -332,14 +332,17 @@ void recurrent_kernel(RecurrentLaunch p) {
     for (int jj = 0; jj < 4; ++jj) wt[jj] = (jj >= 4 - K) ? (float)rw[it][jj] : 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 3; ++jj) win[jj] = (K - 4 + jj >= 0) ? (float)rr3[it][jj] : 0.0f;
+    // (a guarded body per row rather than an exit from the unrolled loop: the exit
+    // sends the row arrays of some instances to scratch memory)
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
-      if (r >= nrows) break;
-      const float xv = (float)rx[it][r];
-      s_qkv[r][slot] = silu(wt[0] * win[0] + wt[1] * win[1] + wt[2] * win[2] + wt[3] * xv);
-      win[0] = win[1];
-      win[1] = win[2];
-      win[2] = xv;
+      if (r < nrows) {
+        const float xv = (float)rx[it][r];
+        s_qkv[r][slot] = silu(wt[0] * win[0] + wt[1] * win[1] + wt[2] * win[2] + wt[3] * xv);
+        win[0] = win[1];
+        win[1] = win[2];
+        win[2] = xv;
+      }
     }
     if (kAdvancesRing) {  // the conv state becomes the last K-1 rows of [conv state ; rows]
 #pragma unroll
