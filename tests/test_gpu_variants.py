@@ -427,3 +427,30 @@ def test_extreme_raw_gates_and_f16_shapes():
             assert slice_err(host(out).reshape(6, dims.Hv, dims.dv), r["out"], np.arange(6)) < TOL_OUT
         assert slice_err(ds.h_host(), S) < TOL_STATE_F16
         assert np.array_equal(ds.ring_host(), ring)
+
+
+@pytest.mark.parametrize("case", ["config3", "d64_g4"])
+def test_woa_bf16_store_and_deterministic(case):
+    """The write-on-accept verify's bf16 output is the round-to-nearest-even of its fp32
+    output on the same inputs (pairs of columns per store at d = 128, single columns at
+    d = 64), and two runs agree bit for bit; the call writes no state."""
+    if case == "config3":
+        d = W.config(3)
+    else:
+        d = W.verify_inputs(3131, 7, W.Dims(Hk=2, Hv=8, dk=64, dv=64, K=4), act="bf16")
+    dims, act = d["dims"], act_dtype(d)
+    T = int(d["cu"][-1])
+    x, w = tdev(d["x"], act), tdev(d["conv_w"], act)
+    a, b = tdev(d["a"], torch.float32), tdev(d["b"], torch.float32)
+    z, nw = tdev(d["z"], act), tdev(d["norm_w"], act)
+    cu_t = tdev(d["cu"], torch.int32)
+    max_k = int(max(2, d["ks"].max()))
+    ds = DeviceStates(d["S0"], d["ring"], act)
+    outs = []
+    for dt in (torch.float32, torch.float32, torch.bfloat16):
+        out = torch.empty((T, dims.Hv * dims.dv), dtype=dt, device=DEV)
+        B.gdn_verify_woa(x, w, ds.ring_ptrs, a, b, ds.h_ptrs, cu_t, max_k, out, dims, z=z, norm_w=nw)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0].to(torch.bfloat16), outs[2])
