@@ -635,7 +635,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 // past it read as zero and stores there are dropped; loads for a later chunk go out
 // right after the last use of the registers they fill and stay raw until used.
 constexpr int kCB = 16;  // state columns of one column tile
-// 32-column workgroups once 16-column ones would exceed twice this many
+// 32-column workgroups once 16-column ones would exceed twice this many, 64-column
+// ones once they would exceed four times this many
 constexpr int64_t kSpineWideMinBlocks = 256;
 
 // K or Q row fragments (bf16: one 16-byte word, fp32: two) kept raw until used.
@@ -983,15 +984,25 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
     uint4 qf[NB][KS][NP];  // Q fragments of the tile, all k-steps, hi (, lo); chunk parity
     uint4 mf[NB][2][2];    // MT fragments: chunk parity, token k-step, hi / lo
     float go[NB];          // Gam of token `lane` of the chunk; chunk parity
-    Raw8<TY> vr[NB];       // V of the tile for the chain waves: operand row vm, 8 columns from vc
-    // V of the tile's 16 rows x CB columns, 8 columns per lane.  With 16-column blocks
-    // that takes half the wave: the other lanes read past the descriptor's extent
-    // (zeros, no memory access) and write nothing.
-    constexpr int LPR = CB / 8;  // lanes per row
-    const int vm = (lane / LPR) & 15, vc = 8 * (lane % LPR);
+    // V of the tile's 16 rows x CB columns, 8 columns per lane, in VPS passes of the
+    // wave (two at 64-column blocks).  With 16-column blocks one pass takes half the
+    // wave: the other lanes read past the descriptor's extent (zeros, no memory access)
+    // and write nothing.
+    constexpr int LPR = CB / 8;                              // lanes per row
+    constexpr int VPS = (16 * LPR + kWave - 1) / kWave;      // passes
+    constexpr int RPP = 16 / VPS;                            // rows per pass
+    Raw8<TY> vr[NB][VPS];  // V of the tile for the chain waves: operand rows vm[.], 8 columns from vc
+    const int vc = 8 * (lane % LPR);
     const bool vlane = lane < 16 * LPR;
-    const uint32_t vof = vlane ? ((8 * (vm >> 2) + (vm & 3)) * CD + 2 * Hk * D + h * D + CB * cb + vc) * (uint32_t)sizeof(TY)
-                               : 0x7fff0000u;
+    int vm[VPS];
+    uint32_t vof[VPS];
+#pragma unroll
+    for (int ps = 0; ps < VPS; ++ps) {
+      vm[ps] = ((lane / LPR) & (RPP - 1)) + RPP * ps;
+      vof[ps] = vlane ? ((8 * (vm[ps] >> 2) + (vm[ps] & 3)) * CD + 2 * Hk * D + h * D + CB * cb + vc) *
+                            (uint32_t)sizeof(TY)
+                      : 0x7fff0000u;
+    }
     // the token rows of this wave's tile: the Gam it writes to LDS
     const bool grow = tt == 2 * (lane >> 5) + ((lane >> 2) & 1);
     auto fetch_q = [&](auto par, int c) {
@@ -1002,14 +1013,18 @@ __global__ __launch_bounds__(512) void spine_kernel(PrefillLaunch p, Tables tb, 
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
           qf[PAR % NB][s][pl] = bload16(rq, 2 * (uint32_t)((NP + pl) * kC * D + frag_off(tt, s, KS, lane)));
-      bload(vr[PAR % NB], tile_rows(c, tt), vof);
+#pragma unroll
+      for (int ps = 0; ps < VPS; ++ps) bload(vr[PAR % NB][ps], tile_rows(c, tt), vof[ps]);
       go[PAR % NB] = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(unit_of(c), unit_bytes(D)), (int)(kGamOff + 4 * lane), 0, 0));
     };
     // the chunk's V (in the activation dtype) and Gam to LDS for the chain waves
     auto put_vg = [&](auto par) {
       constexpr int PAR = decltype(par)::value;
-      if (vlane) store_raw(&s_V[tt][vm][vc], vr[PAR % NB]);
+      if (vlane) {
+#pragma unroll
+        for (int ps = 0; ps < VPS; ++ps) store_raw(&s_V[tt][vm[ps]][vc], vr[PAR % NB][ps]);
+      }
       if (grow) s_G[lane] = go[PAR % NB];
     };
     auto fetch_mt = [&](auto par, int c) {
@@ -1109,10 +1124,15 @@ hipError_t launch_prefill_t(const PrefillLaunch &p, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // 16-column blocks while that is what it takes to give every CU a workgroup
-  // (the chunk time of a block is bound by the operands it loads, the same for 16 or
-  // 32 columns); 32-column blocks, half the operand traffic, for larger batches.
+  // (the chunk time of a block is bound by the operands it loads, nearly the same for
+  // 16 or 32 columns); 32-column blocks, half the operand traffic, for larger batches,
+  // and 64-column blocks (a quarter of it, one workgroup per CU for their 123-131 KiB
+  // of LDS) once there are more than 256 of them.
   const int64_t wg16 = (int64_t)p.n * p.geo.Hv * (D / kCB);
-  if (D >= 32 && wg16 > 2 * kSpineWideMinBlocks)
+  if (D >= 64 && wg16 > 4 * kSpineWideMinBlocks)
+    hipLaunchKernelGGL((spine_kernel<D, 4, TY, TO>), dim3((unsigned)(wg16 / 4)), dim3(512), 0, stream, p, tb,
+                       static_cast<const char *>(units), static_cast<const char *>(kq));
+  else if (D >= 32 && wg16 > 2 * kSpineWideMinBlocks)
     hipLaunchKernelGGL((spine_kernel<D, 2, TY, TO>), dim3((unsigned)(wg16 / 2)), dim3(512), 0, stream, p, tb,
                        static_cast<const char *>(units), static_cast<const char *>(kq));
   else

@@ -167,3 +167,18 @@ def test_prefill_bf16_store_and_determinism():
     assert torch.equal(out32, out32b)
     out16, _, _ = _run(d, fused=True, epilogue=True, out_dtype=torch.bfloat16)
     assert torch.equal(out32.to(torch.bfloat16), out16)
+
+
+@pytest.mark.parametrize("dims,act,lens", [
+    (W.Dims(Hk=4, Hv=16, dk=128, dv=128), "bf16", [70, 1, 130, 0, 64, 200, 3, 65, 129, 17, 256, 40]),
+    (W.Dims(Hk=2, Hv=8, dk=64, dv=64), "f32", [5, 64, 33, 0, 1, 97, 128, 12, 70, 2] * 4),
+    (W.Dims(Hk=2, Hv=8, dk=64, dv=64), "bf16", [65, 3, 0, 130, 64, 7, 1, 90, 40, 22] * 2)])
+def test_prefill_many_sequences_wide_blocks(dims, act, lens):
+    """Batches with enough sequences x heads for the spine's wider column blocks
+    (64 columns at d = 128 with 12 sequences, and at d = 64 with 40; 32 columns at
+    d = 64 with 20), from a y in the activation type; ragged, one-row and empty
+    sequences among them."""
+    d = W.prefill_inputs(6100 + dims.dk + len(lens), lens, dims, act=act)
+    out, ds, y = _run(d, fused=False, epilogue=True, scale=dims.dk ** -0.5)
+    ref = _ref(d, host(y), epilogue=True, scale=dims.dk ** -0.5)
+    _check(d, out, ds, ref, check_ring=False)
